@@ -5,6 +5,11 @@ them; every arithmetic step is one IEEE fp32 operation (NumPy float32),
 rounding of codes is np.rint (half to even), and codes are clamped to the
 format's range.  Groups run along K (the input dimension) of each output row.
 
+Signed zeros: a zero extreme or zero point is taken as +0.0 (IEEE x + 0.0
+turns -0.0 into +0.0), so a group whose minimum is +-0 stores bias +0 and an
+all-non-negative q4k group stores zero point +0 (the superscale review notes
+that zero points are non-negative; the sign of a zero carries no value).
+
 Returned dict (all NumPy arrays, row-major with N leading):
   codes   [N, K]      uint8 (affine, q4k) or int8 (q6k, sym4)
   affine: scales, biases  [N, K/gs]  uint16 bit patterns (fp16 or bf16)
@@ -38,8 +43,10 @@ def quantize_affine(W, f: QFormat):
     reconstruction agree (the superscale page's review notes the same
     principle for its steps); a zero scale gives code 0."""
     G = _groups(W, f.group_size)
-    lo = G.min(axis=2)
-    hi = G.max(axis=2)
+    # "+ 0" turns a -0.0 extreme into +0.0 (signed zeros are canonical +0
+    # in the metadata; see the module notes)
+    lo = G.min(axis=2) + F32(0)
+    hi = G.max(axis=2) + F32(0)
     s32 = (hi - lo) / F32(f.qmax)
     s_bits = to_meta(s32, f.meta)
     b_bits = to_meta(lo, f.meta)
@@ -88,11 +95,11 @@ def quantize_q4k(W, f: QFormat):
     2. Per super-block of 256 (8 groups): scale and zero are each encoded as
        a uint8 code times an fp16 step (step = max / 255)."""
     G = _groups(W, 32)
-    lo = np.minimum(G.min(axis=2), F32(0))
-    hi = np.maximum(G.max(axis=2), F32(0))
+    lo = np.minimum(G.min(axis=2), F32(0)) + F32(0)
+    hi = np.maximum(G.max(axis=2), F32(0)) + F32(0)
     s = (hi - lo) / F32(15)
     with np.errstate(divide="ignore", invalid="ignore"):
-        z = np.where(s != 0, (-lo) / s, F32(0)).astype(np.float32)
+        z = (np.where(s != 0, (-lo) / s, F32(0)) + F32(0)).astype(np.float32)
         t = (G - lo[..., None]) / s[..., None]
     q = np.where(s[..., None] != 0, np.clip(np.rint(t), 0, 15), 0)
     sc, sstep = _encode_per_super(s, 8, 255, 255)

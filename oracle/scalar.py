@@ -47,8 +47,8 @@ def quantize_scalar(W, f: QFormat):
         for n in range(N):
             for g in range(ng):
                 grp = [W[n, g * gs + i] for i in range(gs)]
-                lo = min(grp)
-                hi = max(grp)
+                lo = F32(min(grp) + F32(0))
+                hi = F32(max(grp) + F32(0))
                 s32 = F32(F32(hi - lo) / F32(f.qmax))
                 sb[n, g] = to_meta(np.array([s32]), f.meta)[0]
                 bb[n, g] = to_meta(np.array([lo]), f.meta)[0]
@@ -64,10 +64,10 @@ def quantize_scalar(W, f: QFormat):
         for n in range(N):
             for g in range(ng):
                 grp = [W[n, g * 32 + i] for i in range(32)]
-                lo = min(min(grp), F32(0))
-                hi = max(max(grp), F32(0))
+                lo = F32(min(min(grp), F32(0)) + F32(0))
+                hi = F32(max(max(grp), F32(0)) + F32(0))
                 s = F32(F32(hi - lo) / F32(15))
-                z = F32(0) if s == 0 else F32(F32(-lo) / s)
+                z = F32(0) if s == 0 else F32(F32(F32(-lo) / s) + F32(0))
                 s_all[n, g], z_all[n, g] = s, z
                 for i, w in enumerate(grp):
                     codes[n, g * 32 + i] = 0 if s == 0 else int(
