@@ -1,0 +1,47 @@
+// Internal declarations shared by the host API and the kernel translation
+// units of libqlinear (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qp {
+
+enum Fmt : int { AFFINE = 0, Q4K = 1, Q6K = 2, SYM4 = 3 };
+enum DType : int { F16 = 0, BF16 = 1, F32 = 2 };
+
+// Validated, host-side copy of the descriptor.
+struct Desc {
+  int fmt, bits, gs, sb, meta;
+  int64_t N, K;
+};
+
+struct Bufs {
+  const void* qweight;
+  const void* qweight_hi;
+  const void* scales;
+  const void* zeros;
+  const void* steps;
+};
+
+// Launchers (each returns the hipError_t of its launch).
+hipError_t launch_quantize(const Desc& d, const float* W, void* qweight,
+                           void* qweight_hi, void* scales, void* zeros,
+                           void* steps, hipStream_t s);
+hipError_t launch_unpack(const Desc& d, const Bufs& b, void* codes,
+                         hipStream_t s);
+hipError_t launch_pack(const Desc& d, const void* codes, void* qweight,
+                       void* qweight_hi, hipStream_t s);
+hipError_t launch_dequant(const Desc& d, const Bufs& b, void* out, int out_dt,
+                          hipStream_t s);
+// True when the qGEMV kernel's register plan covers this K (every lane's
+// slice of the activations must fit in registers).
+bool gemv_supported(const Desc& d);
+hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M,
+                       const Bufs& b, const void* bias, void* y, int ydt,
+                       hipStream_t s);
+hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
+                       const Bufs& b, const void* bias, void* y, int ydt,
+                       hipStream_t s);
+
+}  // namespace qp

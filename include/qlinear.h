@@ -1,0 +1,199 @@
+/*
+ * qlinear.h -- C ABI of the group-wise weight-only quantized linear layer
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ *   y[m, n] = sum_k x[m, k] * w[n, k]  (+ bias[n])        (y = x W^T)
+ * where W [N, K] is stored quantized in one of four formats and w is its
+ * dequantized value.  The formats and their dequantization rules:
+ *
+ *   QP_FMT_AFFINE  MLX-style group affine codes (HF Transformers "Metal"
+ *                  quantization page: weights packed into uint32 tensors with
+ *                  per-group scales and biases, bits 2/4/8, group size default
+ *                  64, fused dequantize + matmul "affine_qmm_t"):
+ *                      w = q * scale + bias,  q unsigned b-bit.
+ *   QP_FMT_Q4K     Q4_K-style nested "superscale" int4 (ExecuTorch PR #20571,
+ *                  "Quant schema update", int4 bullet): group 32, super-block
+ *                  256; scale = uint8 code * fp16 step, zero = uint8 code *
+ *                  fp16 step, the two steps of a super-block packed in one
+ *                  32-bit word; 4.625 bits per weight:
+ *                      w = (q - zc*zstep) * (sc*sstep),  q in [0, 15].
+ *   QP_FMT_Q6K     Q6_K-style symmetric int6 (same page, int6 bullet): group
+ *                  16, super-block 256, scale = int8 code * fp16 step, no
+ *                  zero; 6.5625 bits per weight:
+ *                      w = q * (sc*step),  q in [-32, 31], sc in [0, 127].
+ *   QP_FMT_SYM4    symmetric int4 in an int8 carrier, qmin = -7, qmax = 7
+ *                  (ExecuTorch PR #16577, description), fp32 scale per output
+ *                  channel (group_size = K) or per group:
+ *                      w = q * scale.
+ *
+ * Quantization rules (qpack_quantize) -- per group along K of each row, every
+ * step one IEEE fp32 operation, codes rounded half-to-even and clamped:
+ *   AFFINE: lo = min w, hi = max w; scale = meta(fl32(fl32(hi-lo)/(2^b-1)));
+ *           bias = meta(lo); q = scale == 0 ? 0 :
+ *           clamp(rint(fl32(fl32(w - bias)/scale)), 0, 2^b-1), using the
+ *           stored (meta-rounded) scale and bias.
+ *   Q4K:    lo = min(min w, 0), hi = max(max w, 0); s = fl32(fl32(hi-lo)/15);
+ *           z = fl32(-lo/s); q = clamp(rint(fl32(fl32(w-lo)/s)), 0, 15)
+ *           (s == 0 -> q = z = 0).  Then per super-block of 256:
+ *           sstep = fp16(fl32(max s / 255)), sc = clamp(rint(fl32(s/sstep)),
+ *           0, 255) (0 if sstep == 0); zstep, zc likewise from z.
+ *   Q6K:    s = fl32(max|w| / 31); q = clamp(rint(fl32(w/s)), -32, 31);
+ *           step = fp16(fl32(max s / 127)), sc = clamp(rint(fl32(s/step)),
+ *           0, 127).
+ *   SYM4:   s = fl32(max|w| / 7) (fp32, stored); q = clamp(rint(fl32(w/s)),
+ *           -7, 7).
+ *   fp16 conversions keep subnormals (the nested steps usually are).
+ *
+ * Storage (all buffers row-major, N leading, caller-owned device memory):
+ *   qweight     uint32 [N, K*b/32]: code k of a row at word k/(32/b), bits
+ *               [b*(k % (32/b)), +b) -- least-significant first along K.
+ *               SYM4 stores u = q + 8.  Q6K: low nibble of u = q + 32,
+ *               [N, K/8].
+ *   qweight_hi  Q6K only: high 2 bits of u = q + 32, uint32 [N, K/16], same
+ *               bit order.  NULL otherwise.
+ *   scales      AFFINE: fp16|bf16 [N, K/gs];  Q4K: uint8 [N, K/32];
+ *               Q6K: int8 [N, K/16];  SYM4: fp32 [N, K/gs].
+ *   zeros       AFFINE: biases fp16|bf16 [N, K/gs];  Q4K: uint8 zero codes
+ *               [N, K/32];  NULL otherwise.
+ *   steps       Q4K: uint32 [N, K/256], low 16 bits = fp16 scale step, high
+ *               16 bits = fp16 zero step;  Q6K: fp16 [N, K/256];  NULL
+ *               otherwise.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *   * Pointers to weights, activations and outputs are device pointers and
+ *     must be 16-byte aligned; the caller owns every buffer; the library
+ *     keeps no state between calls apart from the per-thread error message.
+ *   * `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *     enqueued asynchronously; a status other than QP_OK means that nothing
+ *     was enqueued and qpack_last_error() names the reason.
+ *   * Validation happens on the host before any launch: shape divisibility
+ *     (K % group_size, whole 16-byte chunks of codes along K, K % 256 for the
+ *     nested formats), supported (fmt, bits, group_size, dtype) combinations,
+ *     alignment, N, K, M > 0.
+ *   * Inputs must be finite; non-finite weights or activations give
+ *     unspecified results.  Activations are used exactly when fp16 / bf16
+ *     values; see qlinear_forward for the one exception.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QP_ABI_VERSION 1
+
+typedef enum {
+  QP_OK = 0,
+  QP_EINVAL = 1,        /* NULL descriptor/pointer, bad enum value          */
+  QP_ESHAPE = 2,        /* N, K, M or group sizes that do not tile          */
+  QP_EUNSUPPORTED = 3,  /* valid but not implemented combination           */
+  QP_EALIGN = 4,        /* a pointer is not 16-byte aligned                 */
+  QP_EHIP = 5           /* the HIP runtime reported an error at launch      */
+} qp_status;
+
+typedef enum {
+  QP_FMT_AFFINE = 0,
+  QP_FMT_Q4K = 1,
+  QP_FMT_Q6K = 2,
+  QP_FMT_SYM4 = 3
+} qp_format;
+
+typedef enum { QP_F16 = 0, QP_BF16 = 1, QP_F32 = 2 } qp_dtype;
+
+/* Which kernel family qlinear_forward_kernel uses. */
+typedef enum {
+  QP_KERNEL_AUTO = 0,   /* qGEMV for M <= 8, qGEMM otherwise                */
+  QP_KERNEL_GEMV = 1,   /* decode-shaped kernel, any M (processed 8 at once) */
+  QP_KERNEL_GEMM = 2    /* prefill-shaped MFMA kernel, any M                 */
+} qp_kernel;
+
+typedef struct {
+  int32_t fmt;          /* qp_format                                         */
+  int32_t bits;         /* AFFINE: 2, 4 or 8; Q4K: 4; Q6K: 6; SYM4: 4         */
+  int32_t group_size;   /* AFFINE: 32, 64, 128; Q4K: 32; Q6K: 16;
+                           SYM4: K (per output channel) or 32, 64, 128       */
+  int32_t super_block;  /* Q4K, Q6K: 256; AFFINE, SYM4: 0                     */
+  int32_t meta_dtype;   /* AFFINE: QP_F16 or QP_BF16; others: ignored         */
+  int32_t reserved;     /* must be 0                                         */
+  int64_t N;            /* output features (rows of W)                       */
+  int64_t K;            /* input features (columns of W)                     */
+} qp_desc;
+
+typedef struct {
+  void* qweight;
+  void* qweight_hi;
+  void* scales;
+  void* zeros;
+  void* steps;
+} qp_weights;
+
+/* Version of this ABI (QP_ABI_VERSION). */
+int32_t qpack_abi_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on the same thread. */
+const char* qpack_last_error(void);
+
+/* Host only.  Byte sizes of the five buffers {qweight, qweight_hi, scales,
+ * zeros, steps} for `d` (0 for an unused buffer).  Bits per weight of the
+ * layout = 8 * sum(bytes) / (N*K): 4.625 for Q4K and 6.5625 for Q6K (the
+ * superscale page's accounting), b + 32/gs for AFFINE. */
+qp_status qpack_sizes(const qp_desc* d, size_t bytes_out[5]);
+
+/* Quantize W (device fp32 [N, K], row-major) into `out`, whose buffers must
+ * have the sizes qpack_sizes gives.  Bit-exact with the rules above. */
+qp_status qpack_quantize(const qp_desc* d, const float* W, const qp_weights* out,
+                         void* stream);
+
+/* Expand the packed codes of `w` into `codes` (device [N, K] bytes): uint8
+ * q for AFFINE and Q4K, int8 q for Q6K and SYM4 (SYM4 gives the int8 carrier
+ * form of the a8w4 page, values in [-7, 7]). */
+qp_status qpack_unpack_codes(const qp_desc* d, const qp_weights* w, void* codes,
+                             void* stream);
+
+/* Pack codes (device [N, K] bytes, as qpack_unpack_codes writes them) into
+ * out->qweight (and out->qweight_hi for Q6K); metadata buffers are not
+ * touched.  Codes outside the format's range are masked to the field width
+ * (unspecified result, no error). */
+qp_status qpack_pack_codes(const qp_desc* d, const void* codes,
+                           const qp_weights* out, void* stream);
+
+/* Dequantize into W_out (device [N, K] of out_dtype).  QP_F32 gives the fp32
+ * evaluation of the format's rule in the order written above (exact for Q6K;
+ * the exact value rounded once for AFFINE and SYM4; for Q4K the difference
+ * q - zero is rounded once before the product).  QP_F16 / QP_BF16 round that
+ * fp32 value to nearest-even. */
+qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out,
+                           int32_t out_dtype, void* stream);
+
+/* y [M, N] (y_dtype, row-major) = x [M, K] (x_dtype, row-major) * W^T
+ * (+ bias [N], x_dtype, or NULL).  x_dtype: QP_F16 or QP_BF16.  y_dtype:
+ * QP_F16, QP_BF16 or QP_F32.  Accumulation is fp32.
+ * M <= 8 runs the decode-shaped qGEMV: codes are used exactly and each
+ * group's scale and offset are applied in fp32.  M > 8 runs the
+ * prefill-shaped qGEMM on fp16 MFMA: weights are dequantized in fp32, rounded
+ * once to fp16 inside the kernel, and activations are converted to fp16
+ * (exact for bf16 values of magnitude in [2^-17, 65504]; larger magnitudes
+ * are unsupported in that path). */
+qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype,
+                          int64_t M, const qp_weights* w, const void* bias,
+                          void* y, int32_t y_dtype, void* stream);
+
+/* qlinear_forward with the kernel family chosen by the caller (qp_kernel). */
+qp_status qlinear_forward_kernel(const qp_desc* d, const void* x,
+                                 int32_t x_dtype, int64_t M,
+                                 const qp_weights* w, const void* bias, void* y,
+                                 int32_t y_dtype, int32_t kernel, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLINEAR_H */

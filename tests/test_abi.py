@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/qlinear.h, and validates arguments on the host
+(every error path returns a status and a message before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_weight_only_qlinear_amd import qlinear
+    return qlinear
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qlinear.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(q):
+    names = declared_functions()
+    assert set(names) == set(q.EXPORTED)
+    for n in names:
+        assert hasattr(q.lib, n)
+    assert q.lib.qpack_abi_version() == 1
+
+
+def test_sizes_and_bpw(q):
+    D = q.QDesc
+    cases = [(D.q4k(256, 4096), 4.625), (D.q6k(256, 4096), 6.5625),
+             (D.affine(256, 4096, 4, 64), 4.5), (D.affine(256, 4096, 2, 64), 2.5),
+             (D.affine(256, 4096, 8, 64), 8.5), (D.sym4(256, 4096), 4 + 32 / 4096)]
+    for d, bpw in cases:
+        s = q.qpack_sizes(d)
+        assert 8 * sum(s.values()) / (d.N * d.K) == bpw
+
+
+def test_sizes_match_oracle(q):
+    import oracle
+    from helpers import qformat_of
+    D = q.QDesc
+    for d in [D.q4k(7, 512), D.q6k(3, 768), D.affine(5, 640, 2, 32, "f16"),
+              D.affine(9, 384, 8, 128), D.sym4(4, 96), D.sym4(4, 256, 64)]:
+        assert q.qpack_sizes(d) == oracle.buffer_bytes(qformat_of(d), d.N, d.K)
+
+
+FAKE = 1 << 20   # an aligned, never-dereferenced address (validation fails first)
+
+
+def _call_forward(q, desc, x=FAKE, xdt=1, M=1, w=None, bias=None, y=FAKE, ydt=1, kernel=0):
+    d = desc.c() if hasattr(desc, "c") else desc
+    if w is None:
+        w = q._Weights(FAKE, FAKE, FAKE, FAKE, FAKE)
+    return q.lib.qlinear_forward_kernel(ctypes.byref(d), ctypes.c_void_p(x), xdt, M,
+                                        ctypes.byref(w), ctypes.c_void_p(bias),
+                                        ctypes.c_void_p(y), ydt, kernel, None)
+
+
+def _err(q):
+    return q.lib.qpack_last_error().decode()
+
+
+@pytest.mark.parametrize("desc,status,msg", [
+    (dict(fmt=0, bits=3, group_size=64, N=8, K=512), 3, "bits"),
+    (dict(fmt=0, bits=4, group_size=48, N=8, K=480), 3, "group_size"),
+    (dict(fmt=0, bits=4, group_size=64, N=8, K=500), 2, "multiple"),
+    (dict(fmt=0, bits=2, group_size=32, N=8, K=96), 2, "16-byte"),
+    (dict(fmt=0, bits=4, group_size=64, N=0, K=512), 2, "positive"),
+    (dict(fmt=0, bits=4, group_size=64, N=8, K=512, meta=2), 3, "meta_dtype"),
+    (dict(fmt=0, bits=4, group_size=64, N=8, K=512, sb=256), 1, "super"),
+    (dict(fmt=1, bits=4, group_size=32, N=8, K=384, sb=256), 2, "256"),
+    (dict(fmt=1, bits=4, group_size=64, N=8, K=512, sb=256), 3, "Q4K"),
+    (dict(fmt=2, bits=6, group_size=32, N=8, K=512, sb=256), 3, "Q6K"),
+    (dict(fmt=2, bits=6, group_size=16, N=8, K=272, sb=256), 2, "256"),
+    (dict(fmt=3, bits=4, group_size=48, N=8, K=96), 3, "SYM4"),
+    (dict(fmt=3, bits=4, group_size=96, N=8, K=100), 2, "32"),
+    (dict(fmt=7, bits=4, group_size=64, N=8, K=512), 1, "format"),
+    (dict(fmt=0, bits=4, group_size=64, N=8, K=512, reserved=1), 1, "reserved"),
+])
+def test_descriptor_validation(q, desc, status, msg):
+    d = q._Desc(desc["fmt"], desc["bits"], desc["group_size"], desc.get("sb", 0),
+                desc.get("meta", 1), desc.get("reserved", 0), desc["N"], desc["K"])
+    out = (ctypes.c_size_t * 5)()
+    st = q.lib.qpack_sizes(ctypes.byref(d), out)
+    assert st == status, _err(q)
+    assert msg.lower() in _err(q).lower()
+    # the same check guards every entry point that takes a descriptor
+    assert _call_forward(q, d) == status
+
+
+def test_forward_argument_validation(q):
+    d = q.QDesc.affine(64, 512)
+    assert _call_forward(q, d, M=0) == q.QP_ESHAPE and "M" in _err(q)
+    assert _call_forward(q, d, xdt=2) == q.QP_EINVAL and "x_dtype" in _err(q)
+    assert _call_forward(q, d, ydt=5) == q.QP_EINVAL and "y_dtype" in _err(q)
+    assert _call_forward(q, d, x=0) == q.QP_EINVAL and "x is NULL" in _err(q)
+    assert _call_forward(q, d, y=0) == q.QP_EINVAL and "y is NULL" in _err(q)
+    assert _call_forward(q, d, x=FAKE + 2) == q.QP_EALIGN and "aligned" in _err(q)
+    assert _call_forward(q, d, bias=FAKE + 8) == q.QP_EALIGN
+    assert _call_forward(q, d, kernel=9) == q.QP_EINVAL and "kernel" in _err(q)
+    w = q._Weights(FAKE, None, None, FAKE, None)
+    assert _call_forward(q, d, w=w) == q.QP_EINVAL and "scales" in _err(q)
+    w = q._Weights(FAKE + 4, None, FAKE, FAKE, None)
+    assert _call_forward(q, d, w=w) == q.QP_EALIGN and "qweight" in _err(q)
+    # the nested formats need their step buffer
+    w = q._Weights(FAKE, None, FAKE, FAKE, None)
+    assert _call_forward(q, q.QDesc.q4k(64, 512), w=w) == q.QP_EINVAL and "steps" in _err(q)
+    w = q._Weights(FAKE, None, FAKE, None, FAKE)
+    assert _call_forward(q, q.QDesc.q6k(64, 512), w=w) == q.QP_EINVAL and "qweight_hi" in _err(q)
+    # the MFMA kernel needs K % 64 == 0
+    assert _call_forward(q, q.QDesc.affine(8, 96, 4, 32), kernel=2) == q.QP_EUNSUPPORTED
+
+
+def test_other_entry_points_validate(q):
+    d = q.QDesc.affine(64, 512).c()
+    w = q._Weights(FAKE, None, FAKE, FAKE, None)
+    assert q.lib.qpack_quantize(ctypes.byref(d), None, ctypes.byref(w), None) == q.QP_EINVAL
+    assert q.lib.qpack_quantize(ctypes.byref(d), ctypes.c_void_p(FAKE + 4), ctypes.byref(w),
+                                None) == q.QP_EALIGN
+    assert q.lib.qpack_unpack_codes(ctypes.byref(d), ctypes.byref(w), None, None) == q.QP_EINVAL
+    assert q.lib.qpack_pack_codes(ctypes.byref(d), None, ctypes.byref(w), None) == q.QP_EINVAL
+    assert q.lib.qpack_dequantize(ctypes.byref(d), ctypes.byref(w), ctypes.c_void_p(FAKE), 7,
+                                  None) == q.QP_EINVAL
+    assert "out_dtype" in _err(q)
+    assert q.lib.qpack_sizes(None, None) == q.QP_EINVAL
+    assert q.lib.qpack_sizes(ctypes.byref(d), None) == q.QP_EINVAL
