@@ -1,0 +1,286 @@
+"""Benchmark of the quantized linear layer on one MI355X.
+
+Headline (the JSON line's `value`): decode-shaped qGEMV, int4 affine codes
+with bf16 per-group scale/bias (group 64), M=1, K=4096, N=14336, x bf16 ->
+y bf16.  One step is one decode pass over a stack of `--layers` layers of
+that shape, each with its own weights (32 distinct weight sets, 1.06 GB, so
+that no layer's weights are served from the 256 MB Infinity Cache); the pass
+is captured once as a HIP graph and replayed.  The metric is effective HBM
+GB/s: algorithmic bytes (packed codes + metadata + x + y, each once) per
+second.
+
+Also reported on the same line: the prefill qGEMM (M=2048, K=4096, N=14336,
+int4 affine gs64) in TFLOP/s against the bf16/fp16 dense MFMA peak, the
+other weight formats' qGEMV rates, the dominant kernel's roofline, and the
+CPU oracle timed on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16/bf16 MFMA (256 CU x 2.4 GHz x 4096)
+METRIC = ("qGEMV effective HBM GB/s (% of peak) at M=1; "
+          "qGEMM TFLOP/s (% MFMA peak) at M=2048")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_layer_weights(q, desc, W_np, copies):
+    """Quantize W on the GPU once, then make `copies` distinct copies."""
+    import torch
+    base = q.qpack_quantize(desc, torch.from_numpy(W_np).cuda())
+    torch.cuda.synchronize()
+    out = [base]
+    for _ in range(copies - 1):
+        out.append({k: (None if v is None else v.clone()) for k, v in base.items()})
+    torch.cuda.synchronize()
+    return out
+
+
+def algorithmic_bytes(q, desc, M):
+    s = q.qpack_sizes(desc)
+    return sum(s.values()) + M * desc.K * 2 + M * desc.N * 2
+
+
+def time_graph(fn_list, steps, warmup):
+    """Capture fn_list (one call per layer) as one graph; replay it.
+    Returns (wall seconds for `steps` replays, event ms for the same)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fn_list:          # eager warm-up outside capture
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fn_list:
+            f()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1)
+
+
+def gemv_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
+    import numpy as np
+    import torch
+    xd = torch.from_numpy(np.ascontiguousarray(x_bits[:M]).view(np.int16)).view(torch.bfloat16).cuda()
+    ws = make_layer_weights(q, desc, W_np, layers)
+    ys = [torch.empty((M, desc.N), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    fns = [(lambda w=w, y=y: q.qlinear_forward(desc, xd, w, out=y)) for w, y in zip(ws, ys)]
+    wall, ev_ms = time_graph(fns, steps, warmup)
+    nb = algorithmic_bytes(q, desc, M)
+    per_launch_s = ev_ms * 1e-3 / (steps * layers)
+    res = dict(bytes_per_call=nb, wall_s=wall, event_ms=ev_ms,
+               us_per_call=per_launch_s * 1e6,
+               gbs=nb / per_launch_s / 1e9,
+               gbs_wall=nb * steps * layers / wall / 1e9,
+               tok_s_per_layer=M / per_launch_s)
+    del ws, ys
+    torch.cuda.empty_cache()
+    return res
+
+
+def gemm_case(q, desc, W_np, x_bits, steps, warmup):
+    import numpy as np
+    import torch
+    M = x_bits.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    w = make_layer_weights(q, desc, W_np, 1)[0]
+    y = torch.empty((M, desc.N), dtype=torch.bfloat16, device="cuda")
+    fns = [lambda: q.qlinear_forward(desc, xd, w, out=y)]
+    wall, ev_ms = time_graph(fns, steps, warmup)
+    per = ev_ms * 1e-3 / steps
+    flops = 2.0 * M * desc.N * desc.K
+    tf = flops / per / 1e12
+    return dict(flops_per_call=flops, us_per_call=per * 1e6, tflops=tf,
+                frac=tf / MFMA_F16_PEAK_TFLOPS, tok_s_per_layer=M / per)
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (NumPy, fp64 dequant + matvec) on the headline workload:
+    whole-layer forwards of K=4096, N=14336 int4 affine, repeated until the
+    time budget is spent (at least one)."""
+    import numpy as np
+    import oracle
+    from oracle import QFormat
+    from bit_weight_only_qlinear_amd import synth
+    wl = synth.make("decode_affine", seed=0)
+    f = QFormat.affine(4, 64, "bf16")
+    qz = oracle.quantize(wl.W, f)
+    x64 = oracle.decode_activations(wl.x_bits, "bf16")
+    N, K = wl.W.shape
+    nbytes = N * K // 2 + 2 * N * (K // 64) * 2 + K * 2 + N * 2
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:
+        threads = 1
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.linear_f64(x64, qz, f)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(nbytes * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{calls} whole-layer forwards (fp64 dequantize + matvec) of "
+                      f"M=1, K=4096, N=14336 int4 affine gs64 in {el:.1f} s; "
+                      f"elementwise NumPy on 1 thread, BLAS on {threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--quick", action="store_true", help="headline case only")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bit_weight_only_qlinear_amd import qlinear as q
+    from bit_weight_only_qlinear_amd import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB read + 1 GiB written")
+        del a, b
+
+    # ---- headline: decode qGEMV int4 affine
+    log("generating decode_affine weights")
+    wl = synth.make("decode_affine", seed=0)
+    N, K = wl.W.shape
+    d4 = q.QDesc.affine(N, K, 4, 64, "bf16")
+    head = gemv_case(q, d4, wl.W, 1, wl.x_bits, args.layers, args.steps, args.warmup)
+    log("headline", head)
+
+    extras = []
+    qgemm = None
+    if not args.quick:
+        for bits in (2, 8):
+            d = q.QDesc.affine(N, K, bits, 64, "bf16")
+            r = gemv_case(q, d, wl.W, 1, wl.x_bits, args.layers, max(20, args.steps // 4),
+                          args.warmup)
+            extras.append(dict(workload=f"decode qGEMV int{bits} affine gs64 M=1 K=4096 N=14336",
+                               gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                               us_per_call=round(r["us_per_call"], 3)))
+            log(extras[-1])
+        del wl
+        log("generating decode_q4k weights")
+        w3 = synth.make("decode_q4k", seed=0)
+        d = q.QDesc.q4k(25600, 5120)
+        r = gemv_case(q, d, w3.W, 1, w3.x_bits, 14, max(20, args.steps // 4), args.warmup)
+        extras.append(dict(workload="decode qGEMV Q4_K-style M=1 K=5120 N=25600",
+                           gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                           us_per_call=round(r["us_per_call"], 3)))
+        log(extras[-1])
+        del w3
+        log("generating decode_8k weights")
+        w4 = synth.make("decode_8k", seed=0, M=8)
+        for dname, d, layers in (("Q6_K-style int6", q.QDesc.q6k(8192, 8192), 19),
+                                 ("sym int4 per-channel", q.QDesc.sym4(8192, 8192), 31)):
+            for M in (1, 4, 8):
+                r = gemv_case(q, d, w4.W, M, w4.x_bits, layers, max(20, args.steps // 4),
+                              args.warmup)
+                extras.append(dict(workload=f"decode qGEMV {dname} M={M} K=8192 N=8192",
+                                   gbs=round(r["gbs"], 1),
+                                   frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                   us_per_call=round(r["us_per_call"], 3)))
+                log(extras[-1])
+        del w4
+        log("generating prefill_affine weights")
+        w5 = synth.make("prefill_affine", seed=0)
+        r = gemm_case(q, q.QDesc.affine(14336, 4096, 4, 64, "bf16"), w5.W, w5.x_bits,
+                      max(10, args.steps // 10), max(3, args.warmup // 4))
+        qgemm = dict(workload="prefill qGEMM int4 affine gs64 M=2048 K=4096 N=14336, "
+                              "fp16 MFMA, fp32 accumulate, bf16 out",
+                     value=round(r["tflops"], 2), unit="TFLOP/s",
+                     peak=MFMA_F16_PEAK_TFLOPS, frac=round(r["frac"], 4),
+                     us_per_call=round(r["us_per_call"], 2),
+                     tok_s_per_layer=round(r["tok_s_per_layer"], 1))
+        log("qgemm", qgemm)
+        del w5
+
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    per_step_s = head["wall_s"] / args.steps
+    value = head["bytes_per_call"] * args.layers * args.steps / head["wall_s"] / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(per_step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded W ~ N(0,0.02) with 4 outlier columns x20, x ~ N(0,1))",
+        "config": {
+            "workload": "decode qGEMV int4 affine gs64 (bf16 scale/bias), M=1, K=4096, "
+                        "N=14336, x bf16, y bf16",
+            "layers_per_step": args.layers,
+            "bytes_per_call": head["bytes_per_call"],
+            "us_per_call": round(head["us_per_call"], 3),
+            "tok_s_per_layer": round(head["tok_s_per_layer"], 1),
+            "graph": "one HIP graph per step",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "qgemm": qgemm,
+        "also": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -255,9 +255,15 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
     return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
   if (kernel == QP_KERNEL_GEMM && !gemm_ok(dd))
     return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 (K=%lld)", (long long)dd.K);
-  const bool gemv_fits = qp::gemv_supported(dd);
+  size_t nbytes[5];
+  sizes_of(dd, nbytes);
+  bool small_bufs = (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
+  for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
+  const bool gemv_fits = qp::gemv_supported(dd) && small_bufs;
   if (kernel == QP_KERNEL_GEMV && !gemv_fits)
-    return fail(QP_EUNSUPPORTED, "K=%lld is too long for the qGEMV kernel", (long long)dd.K);
+    return fail(QP_EUNSUPPORTED,
+                "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
+                (long long)dd.K);
   bool use_gemm;
   if (kernel == QP_KERNEL_AUTO) {
     use_gemm = (M > 8 && gemm_ok(dd)) || !gemv_fits;
@@ -270,7 +276,7 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
   hipError_t e = use_gemm ? qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype,
                                             (hipStream_t)stream)
                           : qp::launch_gemv(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype,
-                                            (hipStream_t)stream);
+                                            nbytes, (hipStream_t)stream);
   return hip_status(e, use_gemm ? "qGEMM launch" : "qGEMV launch");
 }
 

@@ -37,9 +37,11 @@ hipError_t launch_dequant(const Desc& d, const Bufs& b, void* out, int out_dt,
 // True when the qGEMV kernel's register plan covers this K (every lane's
 // slice of the activations must fit in registers).
 bool gemv_supported(const Desc& d);
+// `bytes` are the five buffer sizes of the layout (each < 2 GiB, checked
+// by the caller): the kernel addresses them through buffer resources.
 hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
-                       hipStream_t s);
+                       const size_t bytes[5], hipStream_t s);
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        hipStream_t s);

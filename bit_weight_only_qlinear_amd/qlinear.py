@@ -150,7 +150,11 @@ def alloc_weights(desc: QDesc, device="cuda"):
         if sizes[name]:
             dt = dts[name]
             itemsize = torch.empty(0, dtype=dt).element_size()
-            out[name] = torch.empty(sizes[name] // itemsize, dtype=dt, device=device)
+            # allocated to the next multiple of 16 bytes (the library reads
+            # its buffers in 16-byte units); the view has the exact size
+            padded = (sizes[name] + 15) // 16 * 16
+            out[name] = torch.empty(padded // itemsize, dtype=dt,
+                                    device=device)[: sizes[name] // itemsize]
         else:
             out[name] = None
     return out

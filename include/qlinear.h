@@ -66,6 +66,10 @@
  *   * Pointers to weights, activations and outputs are device pointers and
  *     must be 16-byte aligned; the caller owns every buffer; the library
  *     keeps no state between calls apart from the per-thread error message.
+ *   * Buffers are read in 16-byte units: each input buffer (weights, bias,
+ *     activations) must be allocated up to the next multiple of 16 bytes of
+ *     its size (hipMalloc and torch allocations always are).  Only the
+ *     bytes of the stated size are used.
  *   * `stream` is a hipStream_t (NULL = the default stream).  Work is
  *     enqueued asynchronously; a status other than QP_OK means that nothing
  *     was enqueued and qpack_last_error() names the reason.
