@@ -82,6 +82,42 @@ def time_graph(fn_list, steps, warmup):
     return wall, ev0.elapsed_time(ev1)
 
 
+# Counter summary of the headline kernel: HBM bytes per launch from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading, and
+# the hash of the kernel sources the counters were taken on.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_int4_affine_m1_k4096_n14336.md")
+KERNEL_SOURCES = ("gemv.hip", "device_common.hpp", "qp_internal.hpp")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_weight_only_qlinear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:") or line.startswith("kernel_source_sha256:"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def gemv_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
     import numpy as np
     import torch
@@ -269,11 +305,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
+            "kernel": "k_gemv (int4 affine, one activation row)",
             "achieved": round(head["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "us_per_launch": round(head["us_per_call"], 3),
+            "algorithmic_bytes": head["bytes_per_call"],
+            "traffic": measured_traffic(),
         },
         "cpu_baseline": cpu,
         "qgemm": qgemm,
