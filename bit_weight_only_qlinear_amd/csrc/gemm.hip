@@ -10,10 +10,36 @@
 // bf16 to fp16 in the same staging step (exact for magnitudes in
 // [2^-17, 65504]).
 //
-// Every format dequantizes as w = fma(u, S, T) per group in fp32, with u the
-// stored unsigned field and (S, T) derived from the group metadata:
-//   AFFINE: S = scale, T = bias;  Q4K: S = sc*sstep, T = -S*zc*zstep;
-//   Q6K: S = sc*step, T = -32*S;  SYM4: S = scale, T = -8*S.
+// Design:
+//  * Block tile 256 (n) x 256 (m) x 64 (k), 4 waves in a 2 x 2 grid, each
+//    wave owning 128 x 128 outputs (16 MFMA tiles of 32 x 32, 256 fp32
+//    accumulators per lane).  The weight tile is the MFMA A operand, the
+//    activation tile the B operand, so each lane ends with 4 consecutive
+//    output columns n per row m.
+//  * LDS holds two stages of fp16 tiles (2 x (32 + 32) KiB); each 128-byte
+//    tile row is split into 16-byte chunks stored at chunk ^ (row & 7), so
+//    the 8 lanes of every ds_read_b128 / ds_write_b128 phase hit 8 different
+//    bank groups.
+//  * Global loads are raw buffer loads (rows past M or N read 0) staged two
+//    k-steps ahead in registers: while the MFMAs of step k run, the block
+//    converts step k+1 (already in registers) into the other LDS stage and
+//    the loads of step k+2 are in flight.  One barrier per k-step.
+//  * Dequantization.  Within every 8-column chunk the columns are stored in
+//    the order (0,4,1,5,2,6,3,7) in both tiles (a contraction does not care
+//    about the order of k, as long as both operands agree), which is the
+//    order in which a packed int4 word yields fp16 pairs: (w >> 4i) &
+//    0x000F000F | 0x64006400 is the fp16 pair (1024 + q_i, 1024 + q_{i+4}).
+//    Affine int4 then takes one packed subtract and one packed fma per pair:
+//    w = fma(q, scale, bias) in fp16, a single rounding of the exact weight
+//    when scale and bias are fp16-exact (any bf16 of magnitude >= 2^-14 is).
+//    The other formats use w = fma(u, S, T) in fp32 with u the stored
+//    unsigned field, rounded once to fp16:
+//      AFFINE: S = scale, T = bias;  Q4K: S = sc*sstep, T = -S*zc*zstep;
+//      Q6K: S = sc*step, T = -32*S;  SYM4: S = scale, T = -8*S.
+//  * Tiles are handed out so that each XCD works on a contiguous run of
+//    tiles (shared L2).
+#include <utility>
+
 #include "device_common.hpp"
 #include "qp_internal.hpp"
 
@@ -21,215 +47,415 @@ namespace qp {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDA = BK + 8;  // padded LDS row (halves): 144 B, breaks bank aliasing
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr uint32_t kTileBytes = 256u * BK * 2u;   // one fp16 tile (32 KiB)
+// LDS: weight tiles of stages 0 and 1, then activation tiles of stages 0, 1
+// -- every address is a per-lane base plus an immediate below 64 KiB
+constexpr uint32_t kXBase = 2u * kTileBytes;
+
+enum GKind : int { G_AFF2 = 0, G_AFF4 = 1, G_AFF8 = 2, G_Q4K = 3, G_Q6K = 4, G_SYM4 = 5 };
+
+// Packed code words per weight row per 64-column step (W), and Q6K high
+// plane words (H).
+template <int KIND> struct GT { static constexpr int W = 8, H = 0; };
+template <> struct GT<G_AFF2> { static constexpr int W = 4, H = 0; };
+template <> struct GT<G_AFF8> { static constexpr int W = 16, H = 0; };
+template <> struct GT<G_Q6K> { static constexpr int W = 8, H = 4; };
 
 struct GemmArgs {
-  const uint32_t* qw;
-  const uint32_t* qh;
+  const void* qw;
+  const void* qh;
   const void* scales;
   const void* zeros;
   const void* steps;
-  const uint16_t* x;
-  const uint16_t* bias;
+  const void* x;
+  const void* bias;
   void* y;
   int64_t M, N, K;
-  int fmt, bits, gs, meta_bf16, xbf16, ydt;
-  int tilesM, tilesN;
+  int gs, ydt, tilesM, tilesN;
 };
 
-__device__ __forceinline__ float xval(uint32_t bits, int xbf16) {
-  return xbf16 ? bf16_to_f32(bits) : f16_to_f32(bits);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Per-group (S, T) of the weight row n at column k.
-__device__ __forceinline__ void group_st(const GemmArgs& a, int64_t n, int64_t k, float& S,
-                                         float& T) {
-  if (a.fmt == AFFINE) {
-    const int64_t g = n * (a.K / a.gs) + k / a.gs;
-    S = meta_to_f32(static_cast<const uint16_t*>(a.scales)[g], a.meta_bf16);
-    T = meta_to_f32(static_cast<const uint16_t*>(a.zeros)[g], a.meta_bf16);
-  } else if (a.fmt == Q4K) {
-    const int64_t g = n * (a.K / 32) + k / 32;
-    const uint32_t st = static_cast<const uint32_t*>(a.steps)[n * (a.K / 256) + k / 256];
-    S = (float)static_cast<const uint8_t*>(a.scales)[g] * f16_to_f32(st & 0xFFFFu);
-    const float Z = (float)static_cast<const uint8_t*>(a.zeros)[g] * f16_to_f32(st >> 16);
-    T = -S * Z;
-  } else if (a.fmt == Q6K) {
-    const int64_t g = n * (a.K / 16) + k / 16;
-    const float step = f16_to_f32(static_cast<const uint16_t*>(a.steps)[n * (a.K / 256) + k / 256]);
-    S = (float)static_cast<const int8_t*>(a.scales)[g] * step;
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, expanded at
+// compile time (register arrays indexed by i stay in registers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const unsigned char* smem, uint32_t off) {
+  return *reinterpret_cast<const T*>(smem + off);
+}
+
+// One k-step of one thread's global data, in registers.
+template <int KIND>
+struct Stage {
+  uint4 x[8];                                 // 8 rows x 8 activations (raw bits)
+  uint32_t w[GT<KIND>::W];                    // codes of the thread's weight row
+  uint32_t h[GT<KIND>::H > 0 ? GT<KIND>::H : 1];
+  uint32_t s0, s1, s2;                        // raw metadata (see load_stage)
+};
+
+// Buffer resources and per-thread offsets of one block.
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t x, w, h, s, z, p;
+  uint32_t xo;       // this thread's activation chunk in row (t >> 3)
+  uint32_t xstride;  // 32 activation rows, bytes
+  uint32_t wo, ho;   // this thread's weight row: codes, Q6K high plane
+  uint32_t so, zo, po;  // ... scales, zeros, steps
+};
+
+// Every offset is a per-lane (voffset) offset, so the buffer range check
+// covers all of it: steps at or past K (the pipeline's two phantom steps)
+// read either the next row's data or 0, never memory outside the buffers.
+template <int KIND, bool GS32>
+__device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int kt,
+                                           Stage<KIND>& st) {
+  const uint32_t xk = (uint32_t)kt * (BK * 2);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    st.x[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, r.xo + (uint32_t)i * r.xstride + xk, 0, 0));
+  constexpr int W = GT<KIND>::W;
+  const uint32_t wk = r.wo + (uint32_t)kt * (W * 4);
+#pragma unroll
+  for (int i = 0; i < W / 4; ++i) {
+    const uint4 v = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.w, wk + 16u * i, 0, 0));
+    st.w[4 * i] = v.x; st.w[4 * i + 1] = v.y; st.w[4 * i + 2] = v.z; st.w[4 * i + 3] = v.w;
+  }
+  st.s0 = st.s1 = st.s2 = 0;
+  if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+    // scale and bias of the step's group(s): two per step when gs == 32
+    if constexpr (GS32) {
+      st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + (uint32_t)kt * 4u, 0, 0);
+      st.s1 = __builtin_amdgcn_raw_buffer_load_b32(r.z, r.zo + (uint32_t)kt * 4u, 0, 0);
+    } else {
+      const uint32_t g = (uint32_t)kt * BK / (uint32_t)a.gs;
+      st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + g * 2u, 0, 0);
+      st.s1 = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo + g * 2u, 0, 0);
+    }
+  } else if constexpr (KIND == G_Q4K) {
+    // two uint8 scale codes, two uint8 zero codes, the super-block step word
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + (uint32_t)kt * 2u, 0, 0);
+    st.s1 = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo + (uint32_t)kt * 2u, 0, 0);
+    st.s2 = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + (uint32_t)(kt / 4) * 4u, 0, 0);
+  } else if constexpr (KIND == G_Q6K) {
+    const uint4 v = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.h, r.ho + (uint32_t)kt * 16u, 0, 0));
+    st.h[0] = v.x; st.h[1] = v.y; st.h[2] = v.z; st.h[3] = v.w;
+    // four int8 scale codes, the super-block fp16 step
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + (uint32_t)kt * 4u, 0, 0);
+    st.s2 = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po + (uint32_t)(kt / 4) * 2u, 0, 0);
+  } else {  // SYM4: fp32 scale(s)
+    if constexpr (GS32) {
+      const uint2 v = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(r.s, r.so + (uint32_t)kt * 8u, 0, 0));
+      st.s0 = v.x; st.s1 = v.y;
+    } else {
+      const uint32_t g = (uint32_t)kt * BK / (uint32_t)a.gs;
+      st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + g * 4u, 0, 0);
+    }
+  }
+}
+
+// (S, T) of group `grp` (0-based within the step) of a stage.
+template <int KIND, bool MBF16, bool GS32>
+__device__ __forceinline__ void group_st(const Stage<KIND>& st, int grp, float& S, float& T) {
+  if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+    const int sh = GS32 ? 16 * grp : 0;
+    const uint32_t sb = (st.s0 >> sh) & 0xFFFFu, tb = (st.s1 >> sh) & 0xFFFFu;
+    S = MBF16 ? bf16_to_f32(sb) : f16_to_f32(sb);
+    T = MBF16 ? bf16_to_f32(tb) : f16_to_f32(tb);
+  } else if constexpr (KIND == G_Q4K) {
+    const float sc = (float)((st.s0 >> (8 * grp)) & 0xFFu);
+    const float zc = (float)((st.s1 >> (8 * grp)) & 0xFFu);
+    S = sc * f16_to_f32(st.s2 & 0xFFFFu);
+    T = -S * (zc * f16_to_f32(st.s2 >> 16));
+  } else if constexpr (KIND == G_Q6K) {
+    const float sc = (float)(int8_t)((st.s0 >> (8 * grp)) & 0xFFu);
+    S = sc * f16_to_f32(st.s2 & 0xFFFFu);
     T = -32.f * S;
   } else {
-    S = static_cast<const float*>(a.scales)[n * (a.K / a.gs) + k / a.gs];
+    S = __uint_as_float((GS32 && grp) ? st.s1 : st.s0);
     T = -8.f * S;
   }
 }
 
-// 32 consecutive codes (row n, columns k..k+31) as unsigned fields.
-struct Codes32 {
-  uint32_t w[8];   // packed words (meaning depends on bits)
-  uint32_t h[2];   // Q6K high plane
-};
+// Unsigned field of element e (0..7) of 8-column chunk j (0..7) of a stage.
+template <int KIND>
+__device__ __forceinline__ uint32_t field(const Stage<KIND>& st, int j, int e) {
+  if constexpr (KIND == G_AFF2) return (st.w[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u;
+  else if constexpr (KIND == G_AFF8) return (st.w[2 * j + (e >> 2)] >> (8 * (e & 3))) & 255u;
+  else if constexpr (KIND == G_Q6K)
+    return ((st.w[j] >> (4 * e)) & 15u) | (((st.h[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u) << 4);
+  else return (st.w[j] >> (4 * e)) & 15u;
+}
 
-__device__ __forceinline__ void load_codes(const GemmArgs& a, int64_t n, int64_t k, bool ok,
-                                           Codes32& c) {
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  half2_t h;
+  h.x = (_Float16)lo;
+  h.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Weight chunk j of the thread's row as 8 fp16 in the order (0,4,1,5,2,6,3,7).
+template <int KIND, bool MBF16, bool GS32>
+__device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j) {
+  int grp = 0;
+  if constexpr (KIND == G_Q6K) grp = j >> 1;                       // gs 16
+  else if constexpr (KIND == G_Q4K) grp = j >> 2;                  // gs 32
+  else grp = GS32 ? (j >> 2) : 0;
+  float S, T;
+  group_st<KIND, MBF16, GS32>(st, grp, S, T);
+  uint32_t p[4];
+  if constexpr (KIND == G_AFF4) {
+    half2_t s2, t2;
+    s2.x = s2.y = (_Float16)S;
+    t2.x = t2.y = (_Float16)T;
+    const half2_t mag = {(_Float16)1024.f, (_Float16)1024.f};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c.w[i] = 0;
-  c.h[0] = c.h[1] = 0;
-  if (!ok) return;
-  const int b = a.fmt == Q6K ? 4 : a.bits;
-  const uint32_t* src = a.qw + (n * a.K + k) * b / 32;
-  if (b == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(src);
-    c.w[0] = v.x; c.w[1] = v.y;
-  } else if (b == 4) {
-    uint4 v = *reinterpret_cast<const uint4*>(src);
-    c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = ((st.w[j] >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+      const half2_t q = __builtin_bit_cast(half2_t, m) - mag;
+      p[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, t2));
+    }
   } else {
-    uint4 v0 = reinterpret_cast<const uint4*>(src)[0];
-    uint4 v1 = reinterpret_cast<const uint4*>(src)[1];
-    c.w[0] = v0.x; c.w[1] = v0.y; c.w[2] = v0.z; c.w[3] = v0.w;
-    c.w[4] = v1.x; c.w[5] = v1.y; c.w[6] = v1.z; c.w[7] = v1.w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      p[i] = pack_f16(fmaf((float)field<KIND>(st, j, i), S, T),
+                      fmaf((float)field<KIND>(st, j, i + 4), S, T));
   }
-  if (a.fmt == Q6K) {
-    uint2 v = *reinterpret_cast<const uint2*>(a.qh + (n * a.K + k) / 16);
-    c.h[0] = v.x; c.h[1] = v.y;
+  return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// 8 activations (raw bits) as fp16 in the order (0,4,1,5,2,6,3,7).
+template <bool XBF16>
+__device__ __forceinline__ uint4 act_chunk(const uint4 u) {
+  if constexpr (XBF16) {
+    // bf16 -> fp32 is a shift; fp32 -> fp16 is exact in range, so the
+    // rounding mode of the packed conversion does not matter
+    auto lo = [](uint32_t v) { return __uint_as_float(v << 16); };
+    auto hi = [](uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); };
+    return make_uint4(pack_f16(lo(u.x), lo(u.z)), pack_f16(hi(u.x), hi(u.z)),
+                      pack_f16(lo(u.y), lo(u.w)), pack_f16(hi(u.y), hi(u.w)));
+  } else {
+    return make_uint4(__builtin_amdgcn_perm(u.z, u.x, 0x05040100u),
+                      __builtin_amdgcn_perm(u.z, u.x, 0x07060302u),
+                      __builtin_amdgcn_perm(u.w, u.y, 0x05040100u),
+                      __builtin_amdgcn_perm(u.w, u.y, 0x07060302u));
   }
 }
 
-__device__ __forceinline__ uint32_t field(const GemmArgs& a, const Codes32& c, int i) {
-  if (a.fmt == Q6K)
-    return ((c.w[i / 8] >> (4 * (i % 8))) & 15u) | (((c.h[i / 16] >> (2 * (i % 16))) & 3u) << 4);
-  if (a.bits == 4) return (c.w[i / 8] >> (4 * (i % 8))) & 15u;
-  if (a.bits == 2) return (c.w[i / 16] >> (2 * (i % 16))) & 3u;
-  return (c.w[i / 4] >> (8 * (i % 4))) & 255u;
+// Part p (0..3) of converting a stage into LDS stage buffer `buf`:
+// activation rows 2p, 2p+1 and weight chunks 2p, 2p+1 of this thread.
+template <int KIND, bool XBF16, bool MBF16, bool GS32>
+__device__ __forceinline__ void convert_part(const Stage<KIND>& st, int p, unsigned char* smem,
+                                             uint32_t buf, int tid) {
+  // activation row (tid >> 3) + 32 i, chunk tid & 7; weight row tid
+  const uint32_t xb = kXBase + (uint32_t)(tid >> 3) * 128u +
+                      (uint32_t)((tid & 7) ^ ((tid >> 3) & 7)) * 16u;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = 2 * p + q;
+    *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 4096u * i)) = act_chunk<XBF16>(st.x[i]);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = 2 * p + q;
+    const uint32_t wb = (uint32_t)tid * 128u + (uint32_t)((j ^ (tid & 7)) * 16);
+    *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16, GS32>(st, j);
+  }
 }
 
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[BM * LDA];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[BN * LDA];
+template <int KIND, bool XBF16, bool MBF16, bool GS32>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 1, wj = wave & 1;   // n half, m half
 
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
-  // give each XCD a contiguous run of tiles (m fastest) to share L2.
+  // give each XCD a contiguous run of tiles (m fastest).
   const int T = a.tilesM * a.tilesN;
   const int bid = blockIdx.x;
   const int tile = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;  // a bijection
   const int tm = tile % a.tilesM, tn = tile / a.tilesM;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t mrows = a.M - m0 < BM ? a.M - m0 : BM;
+  const int64_t nrows = a.N - n0 < BN ? a.N - n0 : BN;
+  const int64_t K = a.K;
 
-  // staging assignment: thread -> (row, 32-column half) of both tiles
-  const int sr = tid >> 1;           // 0..127
-  const int sk = (tid & 1) * 32;     // 0 or 32
-  const int64_t xm = m0 + sr, wn_row = n0 + sr;
-  const bool xok = xm < a.M, wok = wn_row < a.N;
-
-  uint4 xr[4];
-  Codes32 cr;
-  float gS, gT;
-
-  auto gload = [&](int64_t k0) {
-    const uint16_t* xp = a.x + xm * a.K + k0 + sk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      xr[i] = xok ? reinterpret_cast<const uint4*>(xp)[i] : make_uint4(0, 0, 0, 0);
-    load_codes(a, wok ? wn_row : 0, k0 + sk, wok, cr);
-    if (wok) group_st(a, wn_row, k0 + sk, gS, gT);
-    else { gS = 0.f; gT = 0.f; }
-  };
-
-  float16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int KT = (int)(a.K / BK);
-  gload(0);
-  for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    // ---- stage activations (bf16|fp16 -> fp16) and weights (-> fp16)
-    {
-      _Float16* ad = As + sr * LDA + sk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t u[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
-        half8_t h;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          h[t] = (_Float16)xval((u[t / 2] >> (16 * (t % 2))) & 0xFFFFu, a.xbf16);
-        *reinterpret_cast<half8_t*>(ad + 8 * i) = h;
-      }
-      _Float16* bd = Bs + sr * LDA + sk;
-      // groups of 16 (Q6K) may change inside the 32 columns
-      float S1 = gS, T1 = gT;
-      if (a.fmt == Q6K && wok) group_st(a, wn_row, (int64_t)kt * BK + sk + 16, S1, T1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        half8_t h;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int e = 8 * i + t;
-          const float S = e < 16 ? gS : S1, T = e < 16 ? gT : T1;
-          h[t] = (_Float16)fmaf((float)field(a, cr, e), S, T);
-        }
-        *reinterpret_cast<half8_t*>(bd + 8 * i) = h;
-      }
+  // ---- buffer resources of this block's rows (rows past M / N read 0)
+  Rsrc r;
+  {
+    const uint32_t xrow = (uint32_t)(K * 2);
+    r.x = rsrc(static_cast<const unsigned char*>(a.x) + m0 * K * 2, (uint32_t)mrows * xrow);
+    r.xo = (uint32_t)(tid >> 3) * xrow + (uint32_t)(tid & 7) * 16u;
+    r.xstride = 32u * xrow;
+    const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
+    r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
+    r.wo = (uint32_t)(tid * wrow);
+    r.h = r.w;
+    r.ho = 0;
+    if constexpr (KIND == G_Q6K) {
+      r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
+      r.ho = (uint32_t)(tid * (K / 4));
     }
-    __syncthreads();
-    if (kt + 1 < KT) gload((int64_t)(kt + 1) * BK);
-
-    // ---- MFMA over the 4 K-slices of 16
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      half8_t af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const half8_t*>(As + row * LDA + kk * 16 + 8 * (lane >> 5));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const half8_t*>(Bs + row * LDA + kk * 16 + 8 * (lane >> 5));
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    int64_t srow = 0, zrow = 0, prow = 0;   // bytes per weight row
+    if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
+    else if constexpr (KIND == G_Q6K) { srow = K / 16; prow = (K / 256) * 2; }
+    else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
+    else { srow = (K / a.gs) * 2; zrow = srow; }
+    r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
+    r.so = (uint32_t)(tid * srow);
+    r.z = r.s; r.zo = r.so;
+    if (zrow) {
+      r.z = rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow));
+      r.zo = (uint32_t)(tid * zrow);
+    }
+    r.p = r.s; r.po = 0;
+    if (prow) {
+      r.p = rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow));
+      r.po = (uint32_t)(tid * prow);
     }
   }
 
-  // ---- epilogue: D[i][j] of a 32x32 tile sits in lane (j + 32*((i/4)%2)),
-  // register 4*(i/8) + i%4
+  float16_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
-      if (n >= a.N) continue;
-      const float bv = a.bias ? xval(a.bias[n], a.xbf16) : 0.f;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-        if (m >= a.M) continue;
-        const float v = acc[i][j][r] + bv;
-        const int64_t idx = m * a.N + n;
-        if (a.ydt == F32) static_cast<float*>(a.y)[idx] = v;
-        else if (a.ydt == BF16) static_cast<uint16_t*>(a.y)[idx] = (uint16_t)f32_to_bf16_rne(v);
-        else static_cast<uint16_t*>(a.y)[idx] = (uint16_t)f32_to_f16_rne(v);
-      }
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // fragment addresses: lane row (lane & 31), chunk 2s + (lane >> 5) stored
+  // at chunk ^ (row & 7) with row & 7 == lane & 7
+  uint32_t fa[4], fb[4];   // per k-slice bases: weight rows, activation rows of the wave
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t f = (uint32_t)(lane & 31) * 128u + (uint32_t)(((2 * s + (lane >> 5)) ^ (lane & 7)) * 16);
+    fa[s] = f + (uint32_t)wi * 128u * 128u;
+    fb[s] = f + kXBase + (uint32_t)wj * 128u * 128u;
+  }
+
+  const int KT = (int)(K / BK);
+
+  auto mfma_step = [&](uint32_t buf, int s) {
+    half8_t af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const half8_t*>(smem + fa[s] + (buf * kTileBytes + 4096u * i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *reinterpret_cast<const half8_t*>(smem + fb[s] + (buf * kTileBytes + 4096u * j));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
+
+  // One k-step: MFMAs on stage kt (LDS buffer kt & 1), conversion of the
+  // registers of step kt+1 (`nxt`) into the other buffer, loads of step kt+2
+  // into `fre` (whose step kt was converted during the previous k-step).
+  // The last two k-steps load and convert phantom steps KT and KT+1 into
+  // the buffer nobody reads any more (see load_stage); no per-step branch.
+  auto kstep = [&](int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
+    const uint32_t cur = (uint32_t)(kt & 1);
+    load_stage<KIND, GS32>(a, r, kt + 2, fre);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      mfma_step(cur, s);
+      convert_part<KIND, XBF16, MBF16, GS32>(nxt, s, smem, cur ^ 1u, tid);
     }
+    __syncthreads();
+  };
+
+  Stage<KIND> st0, st1;
+  load_stage<KIND, GS32>(a, r, 0, st0);
+  load_stage<KIND, GS32>(a, r, 1, st1);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16, GS32>(st0, p, smem, 0u, tid);
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    kstep(kt, st0, st1);
+    if (kt + 1 < KT) kstep(kt + 1, st1, st0);
+  }
+
+  // ---- epilogue: lane holds rows n = 8g + 4*(lane >> 5) + q (q = 0..3) of
+  // column m = lane & 31 of every 32 x 32 tile, in register 4g + q.
+  // Expanded at compile time with predicated stores, so the accumulators
+  // stay in registers.
+  const bool vec4 = (a.N % 4) == 0;
+  const int ydt = a.ydt;
+  const uint16_t* bias = static_cast<const uint16_t*>(a.bias);
+  // an opaque copy of the lane index keeps the epilogue's addresses and
+  // bias loads from being hoisted above the main loop (register pressure)
+  int el = lane;
+  asm volatile("" : "+v"(el));
+  static_for<4>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    static_for<4>([&](auto G) {
+      constexpr int g = decltype(G)::value;
+      const int64_t n = n0 + wi * 128 + i * 32 + 8 * g + 4 * (el >> 5);
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t nn = n + q < a.N ? n + q : a.N - 1;
+          const uint32_t bb = bias[nn];
+          bv[q] = XBF16 ? bf16_to_f32(bb) : f16_to_f32(bb);   // bias has the x dtype
+        }
+      }
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const int64_t m = m0 + wj * 128 + j * 32 + (el & 31);
+        const int64_t idx = m * a.N + n;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] + bv[q];
+        const bool mok = m < a.M;
+        if (mok && vec4 && n < a.N) {
+          if (ydt == F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.y) + idx) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+            uint32_t h[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              h[q] = ydt == BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + idx) =
+                make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          }
+        } else if (mok && !vec4) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (n + q < a.N) {
+              if (ydt == F32) static_cast<float*>(a.y)[idx + q] = v[q];
+              else static_cast<uint16_t*>(a.y)[idx + q] =
+                  (uint16_t)(ydt == BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]));
+            }
+          }
+        }
+      });
+    });
+  });
 }
 
 }  // namespace
@@ -237,27 +463,44 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs a) {
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
                        const void* bias, void* y, int ydt, hipStream_t s) {
   GemmArgs a;
-  a.qw = static_cast<const uint32_t*>(b.qweight);
-  a.qh = static_cast<const uint32_t*>(b.qweight_hi);
+  a.qw = b.qweight;
+  a.qh = b.qweight_hi;
   a.scales = b.scales;
   a.zeros = b.zeros;
   a.steps = b.steps;
-  a.x = static_cast<const uint16_t*>(x);
-  a.bias = static_cast<const uint16_t*>(bias);
+  a.x = x;
+  a.bias = bias;
   a.y = y;
   a.M = M;
   a.N = d.N;
   a.K = d.K;
-  a.fmt = d.fmt;
-  a.bits = d.bits;
   a.gs = d.gs;
-  a.meta_bf16 = d.meta == BF16;
-  a.xbf16 = xdt == BF16;
   a.ydt = ydt;
   a.tilesM = (int)((M + BM - 1) / BM);
   a.tilesN = (int)((d.N + BN - 1) / BN);
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
-  hipLaunchKernelGGL(k_gemm, dim3(blocks), dim3(256), 0, s, a);
+  const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
+  void (*fn)(GemmArgs) = nullptr;
+  // (kind, x dtype, metadata dtype, two groups per 64-column step)
+#define QP_GEMM_FLAGS(KD, MB, G)                                                 \
+  fn = xb ? k_gemm<KD, true, MB, G> : k_gemm<KD, false, MB, G>;
+#define QP_GEMM_AFF(KD)                                                          \
+  if (mb) { if (g32) { QP_GEMM_FLAGS(KD, true, true) } else { QP_GEMM_FLAGS(KD, true, false) } } \
+  else { if (g32) { QP_GEMM_FLAGS(KD, false, true) } else { QP_GEMM_FLAGS(KD, false, false) } }
+  if (d.fmt == AFFINE) {
+    if (d.bits == 2) { QP_GEMM_AFF(G_AFF2) }
+    else if (d.bits == 4) { QP_GEMM_AFF(G_AFF4) }
+    else { QP_GEMM_AFF(G_AFF8) }
+  } else if (d.fmt == Q4K) {
+    QP_GEMM_FLAGS(G_Q4K, false, false)
+  } else if (d.fmt == Q6K) {
+    QP_GEMM_FLAGS(G_Q6K, false, false)
+  } else {
+    if (g32) { QP_GEMM_FLAGS(G_SYM4, false, true) } else { QP_GEMM_FLAGS(G_SYM4, false, false) }
+  }
+#undef QP_GEMM_AFF
+#undef QP_GEMM_FLAGS
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -152,8 +152,8 @@ def test_gemv_forward(q, N, K, M):
                           with_bias=(i % 2 == 0))
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096)])
-@pytest.mark.parametrize("M", [1, 9, 64, 130])
+@pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768)])
+@pytest.mark.parametrize("M", [1, 9, 64, 130, 300])
 def test_gemm_forward(q, N, K, M):
     for i, d in enumerate(_descs(q, N, K)):
         if K % 64:
