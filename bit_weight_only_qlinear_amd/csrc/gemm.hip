@@ -11,11 +11,12 @@
 // [2^-17, 65504]).
 //
 // Design:
-//  * Block tile 256 (n) x 256 (m) x 64 (k), 4 waves in a 2 x 2 grid, each
-//    wave owning 128 x 128 outputs (16 MFMA tiles of 32 x 32, 256 fp32
-//    accumulators per lane).  The weight tile is the MFMA A operand, the
-//    activation tile the B operand, so each lane ends with 4 consecutive
-//    output columns n per row m.
+//  * Block tile 256 (n) x 256 (m) x 64 (k), 8 waves in a 2 (n) x 4 (m)
+//    grid, each wave owning 128 x 64 outputs (8 MFMA tiles of 32 x 32, 128
+//    fp32 accumulators per lane), two waves per SIMD: while one wave waits on
+//    LDS or converts, the other keeps the matrix core busy.  The weight tile
+//    is the MFMA A operand, the activation tile the B operand, so each lane
+//    ends with 4 consecutive output columns n per row m.
 //  * LDS holds two stages of fp16 tiles (2 x (32 + 32) KiB); each 128-byte
 //    tile row is split into 16-byte chunks stored at chunk ^ (row & 7), so
 //    the 8 lanes of every ds_read_b128 / ds_write_b128 phase hit 8 different
@@ -51,6 +52,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 512;
 constexpr uint32_t kTileBytes = 256u * BK * 2u;   // one fp16 tile (32 KiB)
 // LDS: weight tiles of stages 0 and 1, then activation tiles of stages 0, 1
 // -- every address is a per-lane base plus an immediate below 64 KiB
@@ -59,7 +61,7 @@ constexpr uint32_t kXBase = 2u * kTileBytes;
 enum GKind : int { G_AFF2 = 0, G_AFF4 = 1, G_AFF8 = 2, G_Q4K = 3, G_Q6K = 4, G_SYM4 = 5 };
 
 // Packed code words per weight row per 64-column step (W), and Q6K high
-// plane words (H).
+// plane words (H).  Two threads share a weight row, each taking half.
 template <int KIND> struct GT { static constexpr int W = 8, H = 0; };
 template <> struct GT<G_AFF2> { static constexpr int W = 4, H = 0; };
 template <> struct GT<G_AFF8> { static constexpr int W = 16, H = 0; };
@@ -99,22 +101,25 @@ __device__ __forceinline__ T lds_ld(const unsigned char* smem, uint32_t off) {
   return *reinterpret_cast<const T*>(smem + off);
 }
 
-// One k-step of one thread's global data, in registers.
+// One k-step of one thread's global data, in registers: 4 activation
+// chunks (rows (t >> 3) + 64 i, columns 8 (t & 7) ..), and half of weight row
+// t >> 1 (columns 32 (t & 1) .. + 31) with its metadata.
 template <int KIND>
 struct Stage {
-  uint4 x[8];                                 // 8 rows x 8 activations (raw bits)
-  uint32_t w[GT<KIND>::W];                    // codes of the thread's weight row
-  uint32_t h[GT<KIND>::H > 0 ? GT<KIND>::H : 1];
-  uint32_t s0, s1, s2;                        // raw metadata (see load_stage)
+  uint4 x[4];                                     // raw activation bits
+  uint32_t w[GT<KIND>::W / 2];                    // codes
+  uint32_t h[GT<KIND>::H > 0 ? GT<KIND>::H / 2 : 1];
+  uint32_t s0, s1, s2;                            // raw metadata (see load_stage)
 };
 
 // Buffer resources and per-thread offsets of one block.
 struct Rsrc {
   __amdgpu_buffer_rsrc_t x, w, h, s, z, p;
   uint32_t xo;       // this thread's activation chunk in row (t >> 3)
-  uint32_t xstride;  // 32 activation rows, bytes
-  uint32_t wo, ho;   // this thread's weight row: codes, Q6K high plane
-  uint32_t so, zo, po;  // ... scales, zeros, steps
+  uint32_t xstride;  // 64 activation rows, bytes
+  uint32_t wo, ho;   // this thread's half weight row: codes, Q6K high plane
+  uint32_t so, zo, po;  // start of its row: scales, zeros, steps
+  uint32_t half;     // t & 1
 };
 
 // Every offset is a per-lane (voffset) offset, so the buffer range check
@@ -125,63 +130,56 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int
                                            Stage<KIND>& st) {
   const uint32_t xk = (uint32_t)kt * (BK * 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
     st.x[i] = __builtin_bit_cast(
         uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, r.xo + (uint32_t)i * r.xstride + xk, 0, 0));
   constexpr int W = GT<KIND>::W;
   const uint32_t wk = r.wo + (uint32_t)kt * (W * 4);
+  if constexpr (W == 4) {
+    const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.w, wk, 0, 0));
+    st.w[0] = v.x; st.w[1] = v.y;
+  } else {
 #pragma unroll
-  for (int i = 0; i < W / 4; ++i) {
-    const uint4 v = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.w, wk + 16u * i, 0, 0));
-    st.w[4 * i] = v.x; st.w[4 * i + 1] = v.y; st.w[4 * i + 2] = v.z; st.w[4 * i + 3] = v.w;
+    for (int i = 0; i < W / 8; ++i) {
+      const uint4 v = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(r.w, wk + 16u * i, 0, 0));
+      st.w[4 * i] = v.x; st.w[4 * i + 1] = v.y; st.w[4 * i + 2] = v.z; st.w[4 * i + 3] = v.w;
+    }
   }
   st.s0 = st.s1 = st.s2 = 0;
+  const uint32_t g2 = 2u * (uint32_t)kt + r.half;   // this half's group of 32
   if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
-    // scale and bias of the step's group(s): two per step when gs == 32
-    if constexpr (GS32) {
-      st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + (uint32_t)kt * 4u, 0, 0);
-      st.s1 = __builtin_amdgcn_raw_buffer_load_b32(r.z, r.zo + (uint32_t)kt * 4u, 0, 0);
-    } else {
-      const uint32_t g = (uint32_t)kt * BK / (uint32_t)a.gs;
-      st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + g * 2u, 0, 0);
-      st.s1 = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo + g * 2u, 0, 0);
-    }
+    const uint32_t g = GS32 ? g2 : (uint32_t)kt * BK / (uint32_t)a.gs;
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + g * 2u, 0, 0);
+    st.s1 = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo + g * 2u, 0, 0);
   } else if constexpr (KIND == G_Q4K) {
-    // two uint8 scale codes, two uint8 zero codes, the super-block step word
-    st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + (uint32_t)kt * 2u, 0, 0);
-    st.s1 = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo + (uint32_t)kt * 2u, 0, 0);
+    // uint8 scale code, uint8 zero code, the super-block step word
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b8(r.s, r.so + g2, 0, 0);
+    st.s1 = __builtin_amdgcn_raw_buffer_load_b8(r.z, r.zo + g2, 0, 0);
     st.s2 = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + (uint32_t)(kt / 4) * 4u, 0, 0);
   } else if constexpr (KIND == G_Q6K) {
-    const uint4 v = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.h, r.ho + (uint32_t)kt * 16u, 0, 0));
-    st.h[0] = v.x; st.h[1] = v.y; st.h[2] = v.z; st.h[3] = v.w;
-    // four int8 scale codes, the super-block fp16 step
-    st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + (uint32_t)kt * 4u, 0, 0);
+    const uint2 v = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho + (uint32_t)kt * 16u, 0, 0));
+    st.h[0] = v.x; st.h[1] = v.y;
+    // two int8 scale codes (groups of 16), the super-block fp16 step
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + 2u * g2, 0, 0);
     st.s2 = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po + (uint32_t)(kt / 4) * 2u, 0, 0);
-  } else {  // SYM4: fp32 scale(s)
-    if constexpr (GS32) {
-      const uint2 v = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(r.s, r.so + (uint32_t)kt * 8u, 0, 0));
-      st.s0 = v.x; st.s1 = v.y;
-    } else {
-      const uint32_t g = (uint32_t)kt * BK / (uint32_t)a.gs;
-      st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + g * 4u, 0, 0);
-    }
+  } else {  // SYM4: fp32 scale
+    const uint32_t g = GS32 ? g2 : (uint32_t)kt * BK / (uint32_t)a.gs;
+    st.s0 = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so + g * 4u, 0, 0);
   }
 }
 
-// (S, T) of group `grp` (0-based within the step) of a stage.
-template <int KIND, bool MBF16, bool GS32>
+// (S, T) of group `grp` of a stage's half row (only Q6K has two groups).
+template <int KIND, bool MBF16>
 __device__ __forceinline__ void group_st(const Stage<KIND>& st, int grp, float& S, float& T) {
   if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
-    const int sh = GS32 ? 16 * grp : 0;
-    const uint32_t sb = (st.s0 >> sh) & 0xFFFFu, tb = (st.s1 >> sh) & 0xFFFFu;
+    const uint32_t sb = st.s0 & 0xFFFFu, tb = st.s1 & 0xFFFFu;
     S = MBF16 ? bf16_to_f32(sb) : f16_to_f32(sb);
     T = MBF16 ? bf16_to_f32(tb) : f16_to_f32(tb);
   } else if constexpr (KIND == G_Q4K) {
-    const float sc = (float)((st.s0 >> (8 * grp)) & 0xFFu);
-    const float zc = (float)((st.s1 >> (8 * grp)) & 0xFFu);
+    const float sc = (float)(st.s0 & 0xFFu);
+    const float zc = (float)(st.s1 & 0xFFu);
     S = sc * f16_to_f32(st.s2 & 0xFFFFu);
     T = -S * (zc * f16_to_f32(st.s2 >> 16));
   } else if constexpr (KIND == G_Q6K) {
@@ -189,12 +187,13 @@ __device__ __forceinline__ void group_st(const Stage<KIND>& st, int grp, float& 
     S = sc * f16_to_f32(st.s2 & 0xFFFFu);
     T = -32.f * S;
   } else {
-    S = __uint_as_float((GS32 && grp) ? st.s1 : st.s0);
+    S = __uint_as_float(st.s0);
     T = -8.f * S;
   }
 }
 
-// Unsigned field of element e (0..7) of 8-column chunk j (0..7) of a stage.
+// Unsigned field of element e (0..7) of 8-column chunk j (0..3) of a stage's
+// half row.
 template <int KIND>
 __device__ __forceinline__ uint32_t field(const Stage<KIND>& st, int j, int e) {
   if constexpr (KIND == G_AFF2) return (st.w[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u;
@@ -212,14 +211,11 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 }
 
 // Weight chunk j of the thread's row as 8 fp16 in the order (0,4,1,5,2,6,3,7).
-template <int KIND, bool MBF16, bool GS32>
+template <int KIND, bool MBF16>
 __device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j) {
-  int grp = 0;
-  if constexpr (KIND == G_Q6K) grp = j >> 1;                       // gs 16
-  else if constexpr (KIND == G_Q4K) grp = j >> 2;                  // gs 32
-  else grp = GS32 ? (j >> 2) : 0;
+  const int grp = KIND == G_Q6K ? (j >> 1) : 0;   // Q6K groups hold 16 columns
   float S, T;
-  group_st<KIND, MBF16, GS32>(st, grp, S, T);
+  group_st<KIND, MBF16>(st, grp, S, T);
   uint32_t p[4];
   if constexpr (KIND == G_AFF4) {
     half2_t s2, t2;
@@ -259,36 +255,29 @@ __device__ __forceinline__ uint4 act_chunk(const uint4 u) {
   }
 }
 
-// Part p (0..3) of converting a stage into LDS stage buffer `buf`:
-// activation rows 2p, 2p+1 and weight chunks 2p, 2p+1 of this thread.
-template <int KIND, bool XBF16, bool MBF16, bool GS32>
+// Part p (0..3) of converting a stage into LDS stage buffer `buf`: the
+// thread's activation chunk of row (t >> 3) + 64 p and weight chunk p of its
+// half row.
+template <int KIND, bool XBF16, bool MBF16>
 __device__ __forceinline__ void convert_part(const Stage<KIND>& st, int p, unsigned char* smem,
                                              uint32_t buf, int tid) {
-  // activation row (tid >> 3) + 32 i, chunk tid & 7; weight row tid
   const uint32_t xb = kXBase + (uint32_t)(tid >> 3) * 128u +
                       (uint32_t)((tid & 7) ^ ((tid >> 3) & 7)) * 16u;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i = 2 * p + q;
-    *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 4096u * i)) = act_chunk<XBF16>(st.x[i]);
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int j = 2 * p + q;
-    const uint32_t wb = (uint32_t)tid * 128u + (uint32_t)((j ^ (tid & 7)) * 16);
-    *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16, GS32>(st, j);
-  }
+  *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 8192u * p)) = act_chunk<XBF16>(st.x[p]);
+  const int n = tid >> 1, j = 4 * (tid & 1) + p;
+  const uint32_t wb = (uint32_t)n * 128u + (uint32_t)((j ^ (n & 7)) * 16);
+  *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16>(st, p);
 }
 
 template <int KIND, bool XBF16, bool MBF16, bool GS32>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wi = wave >> 1, wj = wave & 1;   // n half, m half
+  const int wi = wave >> 2, wj = wave & 3;   // n half, m quarter
 
   // XCD-aware tile order: consecutive block ids land on different XCDs, so
   // give each XCD a contiguous run of tiles (m fastest).
@@ -307,15 +296,17 @@ k_gemm(GemmArgs a) {
     const uint32_t xrow = (uint32_t)(K * 2);
     r.x = rsrc(static_cast<const unsigned char*>(a.x) + m0 * K * 2, (uint32_t)mrows * xrow);
     r.xo = (uint32_t)(tid >> 3) * xrow + (uint32_t)(tid & 7) * 16u;
-    r.xstride = 32u * xrow;
+    r.xstride = 64u * xrow;
     const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
     r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
-    r.wo = (uint32_t)(tid * wrow);
+    r.half = (uint32_t)(tid & 1);
+    const int64_t n = tid >> 1;
+    r.wo = (uint32_t)(n * wrow) + r.half * (uint32_t)(GT<KIND>::W * 2);
     r.h = r.w;
     r.ho = 0;
     if constexpr (KIND == G_Q6K) {
       r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
-      r.ho = (uint32_t)(tid * (K / 4));
+      r.ho = (uint32_t)(n * (K / 4)) + r.half * 8u;
     }
     int64_t srow = 0, zrow = 0, prow = 0;   // bytes per weight row
     if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
@@ -323,24 +314,24 @@ k_gemm(GemmArgs a) {
     else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
     else { srow = (K / a.gs) * 2; zrow = srow; }
     r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
-    r.so = (uint32_t)(tid * srow);
+    r.so = (uint32_t)(n * srow);
     r.z = r.s; r.zo = r.so;
     if (zrow) {
       r.z = rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow));
-      r.zo = (uint32_t)(tid * zrow);
+      r.zo = (uint32_t)(n * zrow);
     }
     r.p = r.s; r.po = 0;
     if (prow) {
       r.p = rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow));
-      r.po = (uint32_t)(tid * prow);
+      r.po = (uint32_t)(n * prow);
     }
   }
 
-  float16_t acc[4][4];
+  float16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -351,23 +342,23 @@ k_gemm(GemmArgs a) {
   for (int s = 0; s < 4; ++s) {
     const uint32_t f = (uint32_t)(lane & 31) * 128u + (uint32_t)(((2 * s + (lane >> 5)) ^ (lane & 7)) * 16);
     fa[s] = f + (uint32_t)wi * 128u * 128u;
-    fb[s] = f + kXBase + (uint32_t)wj * 128u * 128u;
+    fb[s] = f + kXBase + (uint32_t)wj * 64u * 128u;
   }
 
   const int KT = (int)(K / BK);
 
   auto mfma_step = [&](uint32_t buf, int s) {
-    half8_t af[4], bf[4];
+    half8_t af[4], bf[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       af[i] = *reinterpret_cast<const half8_t*>(smem + fa[s] + (buf * kTileBytes + 4096u * i));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       bf[j] = *reinterpret_cast<const half8_t*>(smem + fb[s] + (buf * kTileBytes + 4096u * j));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
   };
 
@@ -382,7 +373,7 @@ k_gemm(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       mfma_step(cur, s);
-      convert_part<KIND, XBF16, MBF16, GS32>(nxt, s, smem, cur ^ 1u, tid);
+      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid);
     }
     __syncthreads();
   };
@@ -391,7 +382,7 @@ k_gemm(GemmArgs a) {
   load_stage<KIND, GS32>(a, r, 0, st0);
   load_stage<KIND, GS32>(a, r, 1, st1);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16, GS32>(st0, p, smem, 0u, tid);
+  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16>(st0, p, smem, 0u, tid);
   __syncthreads();
   for (int kt = 0; kt < KT; kt += 2) {
     kstep(kt, st0, st1);
@@ -423,9 +414,9 @@ k_gemm(GemmArgs a) {
           bv[q] = XBF16 ? bf16_to_f32(bb) : f16_to_f32(bb);   // bias has the x dtype
         }
       }
-      static_for<4>([&](auto J) {
+      static_for<2>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        const int64_t m = m0 + wj * 128 + j * 32 + (el & 31);
+        const int64_t m = m0 + wj * 64 + j * 32 + (el & 31);
         const int64_t idx = m * a.N + n;
         float v[4];
 #pragma unroll
@@ -500,7 +491,7 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   }
 #undef QP_GEMM_AFF
 #undef QP_GEMM_FLAGS
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
