@@ -18,9 +18,11 @@
 //    is the MFMA A operand, the activation tile the B operand, so each lane
 //    ends with 4 consecutive output columns n per row m.
 //  * LDS holds two stages of fp16 tiles (2 x (32 + 32) KiB); each 128-byte
-//    tile row is split into 16-byte chunks stored at chunk ^ (row & 7), so
-//    the 8 lanes of every ds_read_b128 / ds_write_b128 phase hit 8 different
-//    bank groups.
+//    tile row is split into 16-byte chunks stored at chunk ^ ((row >> 1) & 7).
+//    gfx950 LDS has 64 banks (256 bytes per clock): two consecutive rows
+//    share one bank line, and this swizzle gives the 16 lanes of every
+//    ds_read_b128 / ds_write_b128 phase 16 different 16-byte bank groups
+//    (a plain chunk ^ (row & 7) leaves every fragment read 2-way conflicted).
 //  * Global loads are raw buffer loads (rows past M or N read 0) staged two
 //    k-steps ahead in registers: while the MFMAs of step k run, the block
 //    converts step k+1 (already in registers) into the other LDS stage and
@@ -53,6 +55,21 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 512;
+#ifndef QP_GEMM_PIN_LOADS
+#define QP_GEMM_PIN_LOADS 0
+#endif
+#ifndef QP_GEMM_ROLL
+#define QP_GEMM_ROLL 1
+#endif
+#ifndef QP_GEMM_SGB
+#define QP_GEMM_SGB 1
+#endif
+#ifndef QP_GEMM_SGB_VALU
+#define QP_GEMM_SGB_VALU 4
+#endif
+#ifndef QP_GEMM_DSW_LATE
+#define QP_GEMM_DSW_LATE 1
+#endif
 constexpr uint32_t kTileBytes = 256u * BK * 2u;   // one fp16 tile (32 KiB)
 // LDS: weight tiles of stages 0 and 1, then activation tiles of stages 0, 1
 // -- every address is a per-lane base plus an immediate below 64 KiB
@@ -103,7 +120,7 @@ __device__ __forceinline__ T lds_ld(const unsigned char* smem, uint32_t off) {
 
 // One k-step of one thread's global data, in registers: 4 activation
 // chunks (rows (t >> 3) + 64 i, columns 8 (t & 7) ..), and half of weight row
-// t >> 1 (columns 32 (t & 1) .. + 31) with its metadata.
+// wrow_of(t) (columns 32 (t & 1) .. + 31) with its metadata.
 template <int KIND>
 struct Stage {
   uint4 x[4];                                     // raw activation bits
@@ -203,6 +220,14 @@ __device__ __forceinline__ uint32_t field(const Stage<KIND>& st, int j, int e) {
   else return (st.w[j] >> (4 * e)) & 15u;
 }
 
+// (t & m) | c in one instruction; m comes from an SGPR, c from a VGPR (one
+// VOP3 operand may be scalar).
+__device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(t), "s"(m), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   half2_t h;
   h.x = (_Float16)lo;
@@ -212,7 +237,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 
 // Weight chunk j of the thread's row as 8 fp16 in the order (0,4,1,5,2,6,3,7).
 template <int KIND, bool MBF16>
-__device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j) {
+__device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j, uint32_t magic) {
   const int grp = KIND == G_Q6K ? (j >> 1) : 0;   // Q6K groups hold 16 columns
   float S, T;
   group_st<KIND, MBF16>(st, grp, S, T);
@@ -224,7 +249,7 @@ __device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j) {
     const half2_t mag = {(_Float16)1024.f, (_Float16)1024.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t m = ((st.w[j] >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+      const uint32_t m = and_or(st.w[j] >> (4 * i), 0x000F000Fu, magic);
       const half2_t q = __builtin_bit_cast(half2_t, m) - mag;
       p[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, t2));
     }
@@ -255,18 +280,27 @@ __device__ __forceinline__ uint4 act_chunk(const uint4 u) {
   }
 }
 
+// Weight row staged by thread t (two threads per row, t & 1 = which half).
+// LDS writes are serviced 8 lanes at a time over 32 banks; mapping the 8
+// lanes of each phase to rows {0, 2, 4, 6} (+ 8k, then {1, 3, 5, 7}) gives
+// them 4 different swizzles, i.e. 8 different bank groups.
+__device__ __forceinline__ int wrow_of(int t) {
+  return 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1);
+}
+
 // Part p (0..3) of converting a stage into LDS stage buffer `buf`: the
 // thread's activation chunk of row (t >> 3) + 64 p and weight chunk p of its
 // half row.
 template <int KIND, bool XBF16, bool MBF16>
 __device__ __forceinline__ void convert_part(const Stage<KIND>& st, int p, unsigned char* smem,
-                                             uint32_t buf, int tid) {
+                                             uint32_t buf, int tid, uint32_t magic) {
+  // activation row (tid >> 3) + 64 p: (row >> 1) & 7 == (tid >> 4) & 7
   const uint32_t xb = kXBase + (uint32_t)(tid >> 3) * 128u +
-                      (uint32_t)((tid & 7) ^ ((tid >> 3) & 7)) * 16u;
+                      (uint32_t)((tid & 7) ^ ((tid >> 4) & 7)) * 16u;
   *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 8192u * p)) = act_chunk<XBF16>(st.x[p]);
-  const int n = tid >> 1, j = 4 * (tid & 1) + p;
-  const uint32_t wb = (uint32_t)n * 128u + (uint32_t)((j ^ (n & 7)) * 16);
-  *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16>(st, p);
+  const int n = wrow_of(tid), j = 4 * (tid & 1) + p;
+  const uint32_t wb = (uint32_t)n * 128u + (uint32_t)((j ^ ((n >> 1) & 7)) * 16);
+  *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16>(st, p, magic);
 }
 
 template <int KIND, bool XBF16, bool MBF16, bool GS32>
@@ -300,7 +334,7 @@ k_gemm(GemmArgs a) {
     const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
     r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
     r.half = (uint32_t)(tid & 1);
-    const int64_t n = tid >> 1;
+    const int64_t n = wrow_of(tid);
     r.wo = (uint32_t)(n * wrow) + r.half * (uint32_t)(GT<KIND>::W * 2);
     r.h = r.w;
     r.ho = 0;
@@ -336,30 +370,24 @@ k_gemm(GemmArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // fragment addresses: lane row (lane & 31), chunk 2s + (lane >> 5) stored
-  // at chunk ^ (row & 7) with row & 7 == lane & 7
+  // at chunk ^ ((row >> 1) & 7) with (row >> 1) & 7 == (lane >> 1) & 7
   uint32_t fa[4], fb[4];   // per k-slice bases: weight rows, activation rows of the wave
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const uint32_t f = (uint32_t)(lane & 31) * 128u + (uint32_t)(((2 * s + (lane >> 5)) ^ (lane & 7)) * 16);
+    const uint32_t f = (uint32_t)(lane & 31) * 128u +
+                       (uint32_t)(((2 * s + (lane >> 5)) ^ ((lane >> 1) & 7)) * 16);
     fa[s] = f + (uint32_t)wi * 128u * 128u;
     fb[s] = f + kXBase + (uint32_t)wj * 64u * 128u;
   }
 
   const int KT = (int)(K / BK);
+  const uint32_t magic = 0x64006400u;   // fp16 pair (1024, 1024), kept in a VGPR
 
-  auto mfma_step = [&](uint32_t buf, int s) {
-    half8_t af[4], bf[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const half8_t*>(smem + fa[s] + (buf * kTileBytes + 4096u * i));
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      bf[j] = *reinterpret_cast<const half8_t*>(smem + fb[s] + (buf * kTileBytes + 4096u * j));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  auto rd_a = [&](uint32_t buf, int s, int i) {
+    return *reinterpret_cast<const half8_t*>(smem + fa[s] + (buf * kTileBytes + 4096u * i));
+  };
+  auto rd_b = [&](uint32_t buf, int s, int j) {
+    return *reinterpret_cast<const half8_t*>(smem + fb[s] + (buf * kTileBytes + 4096u * j));
   };
 
   // One k-step: MFMAs on stage kt (LDS buffer kt & 1), conversion of the
@@ -370,11 +398,73 @@ k_gemm(GemmArgs a) {
   auto kstep = [&](int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
     const uint32_t cur = (uint32_t)(kt & 1);
     load_stage<KIND, GS32>(a, r, kt + 2, fre);
+#if QP_GEMM_PIN_LOADS
+    // keep the loads at the top of the step: a whole step to arrive
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+#if QP_GEMM_ROLL
+    // Rolling fragment prefetch: the next k-slice's B fragments are read at
+    // the start of a slice, and A fragment i is re-read for the next slice
+    // as soon as its two MFMAs have issued, so LDS latency hides behind the
+    // remaining MFMAs instead of stalling every slice.
+    half8_t A[4], B[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[i] = rd_a(cur, 0, i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) B[j] = rd_b(cur, 0, j);
+    static_for<4>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      half8_t Bn[2];
+      if constexpr (s < 3) {
+        Bn[0] = rd_b(cur, s + 1, 0);
+        Bn[1] = rd_b(cur, s + 1, 1);
+      }
+      static_for<4>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[1], acc[i][1], 0, 0, 0);
+        if constexpr (s < 3) A[i] = rd_a(cur, s + 1, i);
+      });
+      if constexpr (s < 3) {
+        B[0] = Bn[0];
+        B[1] = Bn[1];
+      }
+      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic);
+#if QP_GEMM_SGB
+      // instruction order of the slice: B prefetch, then per A fragment two
+      // MFMAs, its re-read and a share of the conversion
+      if constexpr (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      static_for<4>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if constexpr (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, QP_GEMM_SGB_VALU, 0);
+#if QP_GEMM_DSW_LATE
+        // LDS writes after the slice's last fragment read: lgkmcnt is in
+        // order, so a write issued before a read would delay that read's wait
+        if constexpr (i == 3) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+#else
+        if constexpr (i == 1 || i == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+#endif
+      });
+#endif
+    });
+#else
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      mfma_step(cur, s);
-      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid);
+      half8_t af[4], bf[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = rd_a(cur, s, i);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = rd_b(cur, s, j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic);
     }
+#endif
     __syncthreads();
   };
 
@@ -382,7 +472,7 @@ k_gemm(GemmArgs a) {
   load_stage<KIND, GS32>(a, r, 0, st0);
   load_stage<KIND, GS32>(a, r, 1, st1);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16>(st0, p, smem, 0u, tid);
+  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16>(st0, p, smem, 0u, tid, magic);
   __syncthreads();
   for (int kt = 0; kt < KT; kt += 2) {
     kstep(kt, st0, st1);
