@@ -251,7 +251,8 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
   if (!aligned16(x)) return fail(QP_EALIGN, "x is not 16-byte aligned");
   if (!aligned16(y)) return fail(QP_EALIGN, "y is not 16-byte aligned");
   if (bias && !aligned16(bias)) return fail(QP_EALIGN, "bias is not 16-byte aligned");
-  if (kernel != QP_KERNEL_AUTO && kernel != QP_KERNEL_GEMV && kernel != QP_KERNEL_GEMM)
+  if (kernel != QP_KERNEL_AUTO && kernel != QP_KERNEL_GEMV && kernel != QP_KERNEL_GEMM &&
+      kernel != QP_KERNEL_GEMV_MFMA)
     return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
   if (kernel == QP_KERNEL_GEMM && !gemm_ok(dd))
     return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 (K=%lld)", (long long)dd.K);
@@ -260,24 +261,45 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
   bool small_bufs = (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
   for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
   const bool gemv_fits = qp::gemv_supported(dd) && small_bufs;
+  const bool skinny_fits = qp::skinny_supported(dd) && M <= 16 &&
+                           (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
   if (kernel == QP_KERNEL_GEMV && !gemv_fits)
     return fail(QP_EUNSUPPORTED,
                 "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
                 (long long)dd.K);
-  bool use_gemm;
+  if (kernel == QP_KERNEL_GEMV_MFMA && !skinny_fits)
+    return fail(QP_EUNSUPPORTED,
+                "the MFMA qGEMV kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
+                (long long)M, (long long)dd.K);
+  enum { USE_GEMV, USE_SKINNY, USE_GEMM } use;
   if (kernel == QP_KERNEL_AUTO) {
-    use_gemm = (M > 8 && gemm_ok(dd)) || !gemv_fits;
-    if (use_gemm && !gemm_ok(dd))
-      return fail(QP_EUNSUPPORTED, "no kernel supports K=%lld for this format", (long long)dd.K);
+    // the MFMA qGEMV dequantizes each weight once instead of one dot product
+    // per activation row; int6 dequantization is costlier, so it pays from
+    // M = 6 there (measured)
+    const int64_t mfma_from = dd.fmt == qp::Q6K ? 6 : 4;
+    if (M >= mfma_from && M <= 16 && skinny_fits) use = USE_SKINNY;
+    else if (M <= 8 && gemv_fits) use = USE_GEMV;
+    else if (gemm_ok(dd)) use = USE_GEMM;
+    else if (gemv_fits) use = USE_GEMV;
+    else return fail(QP_EUNSUPPORTED, "no kernel supports K=%lld for this format", (long long)dd.K);
   } else {
-    use_gemm = kernel == QP_KERNEL_GEMM;
+    use = kernel == QP_KERNEL_GEMM ? USE_GEMM : kernel == QP_KERNEL_GEMV_MFMA ? USE_SKINNY : USE_GEMV;
   }
   (void)hipGetLastError();
-  hipError_t e = use_gemm ? qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype,
-                                            (hipStream_t)stream)
-                          : qp::launch_gemv(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype,
-                                            nbytes, (hipStream_t)stream);
-  return hip_status(e, use_gemm ? "qGEMM launch" : "qGEMV launch");
+  hipError_t e;
+  const char* what;
+  if (use == USE_GEMM) {
+    e = qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, (hipStream_t)stream);
+    what = "qGEMM launch";
+  } else if (use == USE_SKINNY) {
+    e = qp::launch_skinny(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, (hipStream_t)stream);
+    what = "MFMA qGEMV launch";
+  } else {
+    e = qp::launch_gemv(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, nbytes,
+                        (hipStream_t)stream);
+    what = "qGEMV launch";
+  }
+  return hip_status(e, what);
 }
 
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,

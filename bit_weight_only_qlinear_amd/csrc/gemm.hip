@@ -539,7 +539,308 @@ k_gemm(GemmArgs a) {
   });
 }
 
+// ===========================================================================
+// Skinny MFMA kernel for decode batches, 4 <= M <= 16 (y = x W^T).
+//
+// With per-row dot products every code pair costs M dot instructions; here
+// each weight is dequantized once (as in the qGEMM) and the M activation
+// rows ride in the 16 columns of v_mfma_f32_16x16x32_f16 (columns past M
+// are zero).  A block owns 32 weight rows (two 16-row MFMA tiles); its 8
+// waves take every 8th 128-column block of K, and their partial sums meet in
+// LDS.  In a 128-column block, lane l (r = l & 15, g = l >> 4) covers
+// columns 32 g .. 32 g + 31 of weight row r of each tile and of activation
+// row r: MFMA step t uses its 8-column chunk t, in the same column order
+// (0,4,1,5,2,6,3,7) on both operands.  Lane l holds D[4 g + v][r] of each
+// 16 x 16 tile (v = 0..3).  Weights are dequantized to fp16 as in the qGEMM,
+// except per-channel SYM4: its codes q = u - 8 are exact in fp16 and the
+// fp32 channel scale multiplies the reduced sum (rounding the scale to fp16
+// would bias every weight of a row the same way).
+// ===========================================================================
+constexpr int kSkRows = 32;     // weight rows per block
+constexpr int kSkWaves = 8;     // K splits per block
+constexpr int kSkCols = 128;    // columns per block step
+
+struct SkinnyArgs {
+  const void* qw;
+  const void* qh;
+  const void* scales;
+  const void* zeros;
+  const void* steps;
+  const void* x;
+  const void* bias;
+  void* y;
+  int64_t M, N, K;
+  int gs, ydt;
+};
+
+// One 128-column block of one lane: codes of its two rows (32 columns
+// each), their metadata, and its activation chunks.
+template <int KIND>
+struct SkStage {
+  uint4 x[4];
+  uint32_t w[2][GT<KIND>::W / 2];
+  uint32_t h[2][GT<KIND>::H > 0 ? GT<KIND>::H / 2 : 1];
+  uint32_t s0[2], s1[2], s2[2];
+};
+
+// Unsigned field of element e (0..7) of chunk j (0..3) of a lane's 32 columns.
+template <int KIND>
+__device__ __forceinline__ uint32_t sk_field(const uint32_t* w, const uint32_t* h, int j, int e) {
+  if constexpr (KIND == G_AFF2) return (w[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u;
+  else if constexpr (KIND == G_AFF8) return (w[2 * j + (e >> 2)] >> (8 * (e & 3))) & 255u;
+  else if constexpr (KIND == G_Q6K)
+    return ((w[j] >> (4 * e)) & 15u) | (((h[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u) << 4);
+  else return (w[j] >> (4 * e)) & 15u;
+}
+
+template <int KIND, bool MBF16, bool PERCH>
+__device__ __forceinline__ half8_t sk_weight_frag(const SkStage<KIND>& st, int i, int j,
+                                                  uint32_t magic) {
+  if constexpr (PERCH) {
+    // SYM4 with one fp32 scale per output channel: the MFMA takes the exact
+    // codes q = u - 8 (fp16 1024 + u minus 1032) and the scale is applied
+    // once per output in fp32
+    uint32_t p[4];
+    const half2_t off = {(_Float16)1032.f, (_Float16)1032.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p[e] = __builtin_bit_cast(
+          uint32_t, __builtin_bit_cast(half2_t, and_or(st.w[i][j] >> (4 * e), 0x000F000Fu, magic)) - off);
+    return __builtin_bit_cast(half8_t, make_uint4(p[0], p[1], p[2], p[3]));
+  }
+  float S, T;
+  if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+    const uint32_t sb = st.s0[i] & 0xFFFFu, tb = st.s1[i] & 0xFFFFu;
+    S = MBF16 ? bf16_to_f32(sb) : f16_to_f32(sb);
+    T = MBF16 ? bf16_to_f32(tb) : f16_to_f32(tb);
+  } else if constexpr (KIND == G_Q4K) {
+    S = (float)(st.s0[i] & 0xFFu) * f16_to_f32(st.s2[i] & 0xFFFFu);
+    T = -S * ((float)(st.s1[i] & 0xFFu) * f16_to_f32(st.s2[i] >> 16));
+  } else if constexpr (KIND == G_Q6K) {
+    S = (float)(int8_t)((st.s0[i] >> (8 * (j >> 1))) & 0xFFu) * f16_to_f32(st.s2[i] & 0xFFFFu);
+    T = -32.f * S;
+  } else {
+    S = __uint_as_float(st.s0[i]);
+    T = -8.f * S;
+  }
+  uint32_t p[4];
+  if constexpr (KIND == G_AFF4) {
+    // fp16 pairs of the codes, one packed fma: exact codes, one rounding
+    // (bf16 / fp16 scales and biases are fp16-exact; SYM4's fp32 scale is
+    // not, and rounding it would bias a whole row, so SYM4 stays in fp32)
+    half2_t s2, t2;
+    s2.x = s2.y = (_Float16)S;
+    t2.x = t2.y = (_Float16)T;
+    const half2_t mag = {(_Float16)1024.f, (_Float16)1024.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m = and_or(st.w[i][j] >> (4 * e), 0x000F000Fu, magic);
+      const half2_t q = __builtin_bit_cast(half2_t, m) - mag;
+      p[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, t2));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p[e] = pack_f16(fmaf((float)sk_field<KIND>(st.w[i], st.h[i], j, e), S, T),
+                      fmaf((float)sk_field<KIND>(st.w[i], st.h[i], j, e + 4), S, T));
+  }
+  return __builtin_bit_cast(half8_t, make_uint4(p[0], p[1], p[2], p[3]));
+}
+
+struct SkRsrc {
+  __amdgpu_buffer_rsrc_t x, w, h, s, z, p;
+  uint32_t xo;                          // activation row r, lane's columns (kOOB if r >= M)
+  uint32_t wo[2], ho[2], so[2], zo[2], po[2];
+  uint32_t g;                           // lane >> 4
+};
+
+template <int KIND, bool PERCH>
+__device__ __forceinline__ void sk_load(const SkinnyArgs& a, const SkRsrc& r, int kb,
+                                        SkStage<KIND>& st) {
+  const uint32_t c0 = (uint32_t)kb * kSkCols + 32u * r.g;   // lane's first column
+  // activations: 32 columns = 64 bytes (rows past M read 0)
+  const uint32_t xo = r.xo == 0xFFFFFFFFu ? 0x80000000u : r.xo + 2u * c0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    st.x[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, xo + 16u * t, 0, 0));
+  constexpr int W = GT<KIND>::W;   // code words per 64 columns; a lane takes W / 2
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t wk = r.wo[i] + c0 * (uint32_t)(W / 2) / 8u;   // bytes: c0 * bits / 8
+    if constexpr (W == 4) {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.w, wk, 0, 0));
+      st.w[i][0] = v.x; st.w[i][1] = v.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < W / 8; ++c) {
+        const uint4 v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(r.w, wk + 16u * c, 0, 0));
+        st.w[i][4 * c] = v.x; st.w[i][4 * c + 1] = v.y;
+        st.w[i][4 * c + 2] = v.z; st.w[i][4 * c + 3] = v.w;
+      }
+    }
+    st.s0[i] = st.s1[i] = st.s2[i] = 0;
+    if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+      const uint32_t g = c0 / (uint32_t)a.gs;
+      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so[i] + 2u * g, 0, 0);
+      st.s1[i] = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo[i] + 2u * g, 0, 0);
+    } else if constexpr (KIND == G_Q4K) {
+      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b8(r.s, r.so[i] + c0 / 32u, 0, 0);
+      st.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(r.z, r.zo[i] + c0 / 32u, 0, 0);
+      st.s2[i] = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po[i] + 4u * (c0 / 256u), 0, 0);
+    } else if constexpr (KIND == G_Q6K) {
+      const uint2 v = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho[i] + c0 / 4u, 0, 0));
+      st.h[i][0] = v.x; st.h[i][1] = v.y;
+      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so[i] + c0 / 16u, 0, 0);
+      st.s2[i] = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po[i] + 2u * (c0 / 256u), 0, 0);
+    } else if constexpr (!PERCH) {
+      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so[i] + 4u * (c0 / (uint32_t)a.gs), 0, 0);
+    }
+  }
+}
+
+template <int KIND, bool XBF16, bool MBF16, bool PERCH>
+__global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
+  __shared__ float part[kSkWaves][2][16][17];   // per wave, tile, weight row, activation row
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rr = lane & 15;
+  const int64_t n0 = (int64_t)blockIdx.x * kSkRows;
+  const int64_t nrows = a.N - n0 < kSkRows ? a.N - n0 : kSkRows;
+  const int64_t K = a.K;
+  const int KB = (int)(K / kSkCols);
+
+  SkRsrc r;
+  {
+    r.g = (uint32_t)(lane >> 4);
+    r.x = rsrc(a.x, (uint32_t)(a.M * K * 2));
+    r.xo = rr < a.M ? (uint32_t)(rr * K * 2) : 0xFFFFFFFFu;
+    const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
+    int64_t srow = 0, zrow = 0, prow = 0;
+    if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
+    else if constexpr (KIND == G_Q6K) { srow = K / 16; prow = (K / 256) * 2; }
+    else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
+    else { srow = (K / a.gs) * 2; zrow = srow; }
+    r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
+    r.h = r.w;
+    if constexpr (KIND == G_Q6K)
+      r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
+    r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
+    r.z = zrow ? rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow))
+               : r.s;
+    r.p = prow ? rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow))
+               : r.s;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t n = 16 * i + rr;
+      r.wo[i] = (uint32_t)(n * wrow);
+      r.ho[i] = (uint32_t)(n * (K / 4));
+      r.so[i] = (uint32_t)(n * srow);
+      r.zo[i] = (uint32_t)(n * zrow);
+      r.po[i] = (uint32_t)(n * prow);
+    }
+  }
+
+  typedef float float4_t __attribute__((ext_vector_type(4)));
+  float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const uint32_t magic = 0x64006400u;
+
+  auto compute = [&](const SkStage<KIND>& st) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const half8_t B = __builtin_bit_cast(half8_t, act_chunk<XBF16>(st.x[t]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sk_weight_frag<KIND, MBF16, PERCH>(st, i, t, magic),
+                                                        B, acc[i], 0, 0, 0);
+    }
+  };
+
+  // the wave's column blocks: wave, wave + 8, ...; one block in flight while
+  // the previous one is computed
+  SkStage<KIND> s0, s1;
+  int kb = wave;
+  if (kb < KB) sk_load<KIND, PERCH>(a, r, kb, s0);
+  while (kb < KB) {
+    if (kb + kSkWaves < KB) sk_load<KIND, PERCH>(a, r, kb + kSkWaves, s1);
+    compute(s0);
+    kb += kSkWaves;
+    if (kb >= KB) break;
+    if (kb + kSkWaves < KB) sk_load<KIND, PERCH>(a, r, kb + kSkWaves, s0);
+    compute(s1);
+    kb += kSkWaves;
+  }
+
+  // ---- partial sums of the 8 waves meet in LDS
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[wave][i][4 * (lane >> 4) + v][rr] = acc[i][v];
+  __syncthreads();
+  // thread -> (weight row 0..31, activation row 0..15)
+  const int nl = tid >> 4, m = tid & 15;
+  const int64_t n = n0 + nl;
+  if (m < a.M && n < a.N) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) sum += part[w][nl >> 4][nl & 15][m];
+    if constexpr (PERCH) sum *= static_cast<const float*>(a.scales)[n];
+    if (a.bias) {
+      const uint32_t bb = static_cast<const uint16_t*>(a.bias)[n];
+      sum += XBF16 ? bf16_to_f32(bb) : f16_to_f32(bb);
+    }
+    const int64_t idx = (int64_t)m * a.N + n;
+    if (a.ydt == F32) static_cast<float*>(a.y)[idx] = sum;
+    else static_cast<uint16_t*>(a.y)[idx] =
+        (uint16_t)(a.ydt == BF16 ? f32_to_bf16_rne(sum) : f32_to_f16_rne(sum));
+  }
+}
+
 }  // namespace
+
+bool skinny_supported(const Desc& d) { return d.K % kSkCols == 0; }
+
+hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
+                         const void* bias, void* y, int ydt, hipStream_t s) {
+  if (M < 1 || M > 16 || !skinny_supported(d)) return hipErrorInvalidValue;
+  SkinnyArgs a;
+  a.qw = b.qweight;
+  a.qh = b.qweight_hi;
+  a.scales = b.scales;
+  a.zeros = b.zeros;
+  a.steps = b.steps;
+  a.x = x;
+  a.bias = bias;
+  a.y = y;
+  a.M = M;
+  a.N = d.N;
+  a.K = d.K;
+  a.gs = d.gs;
+  a.ydt = ydt;
+  const bool xb = xdt == BF16, mb = d.meta == BF16;
+  void (*fn)(SkinnyArgs) = nullptr;
+#define QP_SK(KD, MB) fn = xb ? k_skinny<KD, true, MB, false> : k_skinny<KD, false, MB, false>;
+  if (d.fmt == AFFINE) {
+    if (d.bits == 2) { if (mb) { QP_SK(G_AFF2, true) } else { QP_SK(G_AFF2, false) } }
+    else if (d.bits == 4) { if (mb) { QP_SK(G_AFF4, true) } else { QP_SK(G_AFF4, false) } }
+    else { if (mb) { QP_SK(G_AFF8, true) } else { QP_SK(G_AFF8, false) } }
+  } else if (d.fmt == Q4K) {
+    QP_SK(G_Q4K, false)
+  } else if (d.fmt == Q6K) {
+    QP_SK(G_Q6K, false)
+  } else if (d.gs == d.K) {
+    fn = xb ? k_skinny<G_SYM4, true, false, true> : k_skinny<G_SYM4, false, false, true>;
+  } else {
+    QP_SK(G_SYM4, false)
+  }
+#undef QP_SK
+  const unsigned blocks = (unsigned)((d.N + kSkRows - 1) / kSkRows);
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * kSkWaves), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
                        const void* bias, void* y, int ydt, hipStream_t s) {

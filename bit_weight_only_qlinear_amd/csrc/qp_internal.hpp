@@ -42,6 +42,12 @@ bool gemv_supported(const Desc& d);
 hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        const size_t bytes[5], hipStream_t s);
+// Skinny MFMA kernel for 4 <= M <= 16 (any M in 1..16 accepted): K must be a
+// multiple of 128.
+bool skinny_supported(const Desc& d);
+hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M,
+                         const Bufs& b, const void* bias, void* y, int ydt,
+                         hipStream_t s);
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        hipStream_t s);

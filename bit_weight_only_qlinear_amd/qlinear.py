@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libqlinear.so")
 QP_OK, QP_EINVAL, QP_ESHAPE, QP_EUNSUPPORTED, QP_EALIGN, QP_EHIP = range(6)
 QP_FMT_AFFINE, QP_FMT_Q4K, QP_FMT_Q6K, QP_FMT_SYM4 = range(4)
 QP_F16, QP_BF16, QP_F32 = range(3)
-QP_KERNEL_AUTO, QP_KERNEL_GEMV, QP_KERNEL_GEMM = range(3)
+QP_KERNEL_AUTO, QP_KERNEL_GEMV, QP_KERNEL_GEMM, QP_KERNEL_GEMV_MFMA = range(4)
 
 FMT_IDS = {"affine": QP_FMT_AFFINE, "q4k": QP_FMT_Q4K, "q6k": QP_FMT_Q6K,
            "sym4": QP_FMT_SYM4}

@@ -113,9 +113,12 @@ typedef enum { QP_F16 = 0, QP_BF16 = 1, QP_F32 = 2 } qp_dtype;
 
 /* Which kernel family qlinear_forward_kernel uses. */
 typedef enum {
-  QP_KERNEL_AUTO = 0,   /* qGEMV for M <= 8, qGEMM otherwise                */
-  QP_KERNEL_GEMV = 1,   /* decode-shaped kernel, any M (processed 8 at once) */
-  QP_KERNEL_GEMM = 2    /* prefill-shaped MFMA kernel, any M                 */
+  QP_KERNEL_AUTO = 0,      /* M <= 3 (Q6K: M <= 5): qGEMV; up to M = 16: MFMA
+                              qGEMV when K % 128 == 0 (else qGEMV up to M = 8);
+                              larger M: qGEMM                                */
+  QP_KERNEL_GEMV = 1,      /* decode-shaped kernel, any M (processed 8 at once) */
+  QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M               */
+  QP_KERNEL_GEMV_MFMA = 3  /* decode-shaped MFMA kernel, M <= 16, K % 128 == 0 */
 } qp_kernel;
 
 typedef struct {
@@ -180,12 +183,16 @@ qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out,
 /* y [M, N] (y_dtype, row-major) = x [M, K] (x_dtype, row-major) * W^T
  * (+ bias [N], x_dtype, or NULL).  x_dtype: QP_F16 or QP_BF16.  y_dtype:
  * QP_F16, QP_BF16 or QP_F32.  Accumulation is fp32.
- * M <= 8 runs the decode-shaped qGEMV: codes are used exactly and each
- * group's scale and offset are applied in fp32.  M > 8 runs the
- * prefill-shaped qGEMM on fp16 MFMA: weights are dequantized in fp32, rounded
- * once to fp16 inside the kernel, and activations are converted to fp16
- * (exact for bf16 values of magnitude in [2^-17, 65504]; larger magnitudes
- * are unsupported in that path). */
+ * The decode-shaped qGEMV (QP_KERNEL_GEMV) uses the codes exactly and
+ * applies each group's scale and offset in fp32.  The MFMA kernels
+ * (QP_KERNEL_GEMV_MFMA for 4 <= M <= 16, QP_KERNEL_GEMM for larger M) run on
+ * fp16 MFMA: each weight is dequantized and rounded once to fp16 inside the
+ * kernel (scales, zero points and weights are assumed to lie in the fp16
+ * normal range; the MFMA qGEMV feeds per-channel SYM4 codes exactly and
+ * applies the fp32 channel scale to the result), and activations are
+ * converted to fp16 (exact for bf16
+ * values of magnitude in [2^-17, 65504]; larger magnitudes are unsupported
+ * in those paths).  QP_KERNEL_AUTO picks by M as listed under qp_kernel. */
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype,
                           int64_t M, const qp_weights* w, const void* bias,
                           void* y, int32_t y_dtype, void* stream);

@@ -114,6 +114,12 @@ def test_forward_argument_validation(q):
     assert _call_forward(q, q.QDesc.q6k(64, 512), w=w) == q.QP_EINVAL and "qweight_hi" in _err(q)
     # the MFMA kernel needs K % 64 == 0
     assert _call_forward(q, q.QDesc.affine(8, 96, 4, 32), kernel=2) == q.QP_EUNSUPPORTED
+    # the MFMA qGEMV needs K % 128 == 0 and M <= 16
+    assert _call_forward(q, q.QDesc.affine(8, 192, 4, 64), M=4,
+                         kernel=q.QP_KERNEL_GEMV_MFMA) == q.QP_EUNSUPPORTED
+    assert "K % 128" in _err(q)
+    assert _call_forward(q, q.QDesc.affine(8, 256, 4, 64), M=17,
+                         kernel=q.QP_KERNEL_GEMV_MFMA) == q.QP_EUNSUPPORTED
 
 
 def test_other_entry_points_validate(q):

@@ -152,6 +152,19 @@ def test_gemv_forward(q, N, K, M):
                           with_bias=(i % 2 == 0))
 
 
+@pytest.mark.parametrize("N,K", [(1, 256), (31, 384), (77, 1024), (300, 4096), (513, 5120)])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 11, 16])
+def test_gemv_mfma_forward(q, N, K, M):
+    """The skinny MFMA decode kernel on every format, ragged N, M up to 16."""
+    for i, d in enumerate(_descs(q, N, K)):
+        if K % 256 and d.fmt in ("q4k", "q6k"):
+            continue
+        for xdt, ydt in [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16")]:
+            print("gemv_mfma", _id(d), M, xdt, ydt, flush=True)
+            _forward_case(q, d, M, xdt, ydt, q.QP_KERNEL_GEMV_MFMA, seed=N * 37 + K + M + i,
+                          with_bias=(i % 2 == 1))
+
+
 @pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768)])
 @pytest.mark.parametrize("M", [1, 9, 64, 130, 300])
 def test_gemm_forward(q, N, K, M):
