@@ -273,10 +273,15 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
                 (long long)M, (long long)dd.K);
   enum { USE_GEMV, USE_SKINNY, USE_GEMM } use;
   if (kernel == QP_KERNEL_AUTO) {
-    // the MFMA qGEMV dequantizes each weight once instead of one dot product
-    // per activation row; int6 dequantization is costlier, so it pays from
-    // M = 6 there (measured)
-    const int64_t mfma_from = dd.fmt == qp::Q6K ? 6 : 4;
+    // The MFMA qGEMV dequantizes each weight once instead of doing one dot
+    // product per activation row.  Where it takes over (measured on
+    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 3 for
+    // the fp16-dequantized int2/int4 affine and grouped SYM4, 6 for the
+    // fp32-dequantized int8 affine, Q4K and Q6K.
+    int64_t mfma_from = 3;
+    if (dd.fmt == qp::SYM4 && dd.gs == dd.K) mfma_from = 2;
+    else if (dd.fmt == qp::Q4K || dd.fmt == qp::Q6K || (dd.fmt == qp::AFFINE && dd.bits == 8))
+      mfma_from = 6;
     if (M >= mfma_from && M <= 16 && skinny_fits) use = USE_SKINNY;
     else if (M <= 8 && gemv_fits) use = USE_GEMV;
     else if (gemm_ok(dd)) use = USE_GEMM;

@@ -556,8 +556,15 @@ k_gemm(GemmArgs a) {
 // fp32 channel scale multiplies the reduced sum (rounding the scale to fp16
 // would bias every weight of a row the same way).
 // ===========================================================================
-constexpr int kSkRows = 32;     // weight rows per block
-constexpr int kSkWaves = 8;     // K splits per block
+#ifndef QP_SK_WAVES
+#define QP_SK_WAVES 8
+#endif
+#ifndef QP_SK_DEPTH
+#define QP_SK_DEPTH 1
+#endif
+constexpr int kSkRows = 32;             // weight rows per block
+constexpr int kSkWaves = QP_SK_WAVES;   // K splits per block
+constexpr int kSkDepth = QP_SK_DEPTH;   // column blocks in flight ahead of the one computed
 constexpr int kSkCols = 128;    // columns per block step
 
 struct SkinnyArgs {
@@ -759,19 +766,26 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
     }
   };
 
-  // the wave's column blocks: wave, wave + 8, ...; one block in flight while
-  // the previous one is computed
-  SkStage<KIND> s0, s1;
-  int kb = wave;
-  if (kb < KB) sk_load<KIND, PERCH>(a, r, kb, s0);
-  while (kb < KB) {
-    if (kb + kSkWaves < KB) sk_load<KIND, PERCH>(a, r, kb + kSkWaves, s1);
-    compute(s0);
-    kb += kSkWaves;
-    if (kb >= KB) break;
-    if (kb + kSkWaves < KB) sk_load<KIND, PERCH>(a, r, kb + kSkWaves, s0);
-    compute(s1);
-    kb += kSkWaves;
+  // the wave's column blocks: wave, wave + kSkWaves, ...; kSkDepth blocks in
+  // flight ahead of the one being computed (a ring of kSkDepth + 1 stages,
+  // unrolled so every stage index is a compile-time constant)
+  constexpr int R = kSkDepth + 1;
+  SkStage<KIND> st[R];
+  const int J = wave < KB ? (KB - wave + kSkWaves - 1) / kSkWaves : 0;   // blocks of this wave
+  static_for<kSkDepth>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (p < J) sk_load<KIND, PERCH>(a, r, wave + p * kSkWaves, st[p]);
+  });
+  for (int j0 = 0; j0 < J; j0 += R) {
+    static_for<R>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const int j = j0 + q;
+      if (j < J) {
+        if (j + kSkDepth < J)
+          sk_load<KIND, PERCH>(a, r, wave + (j + kSkDepth) * kSkWaves, st[(q + kSkDepth) % R]);
+        compute(st[q]);
+      }
+    });
   }
 
   // ---- partial sums of the 8 waves meet in LDS

@@ -727,15 +727,17 @@ GemvFn pick(int kind, bool xb, int mt, int cpl, int nb) {
 // Chooses the M tile, the K split and the chunks per lane so that the
 // lane's activations fit its register budget (CPL * MT chunks of 16
 // activation pairs; fewer for 2-bit codes, which have 32 pairs per chunk, and
-// for int6, which carries a second code plane); one chunk per lane always
-// fits.  Shrinks the M tile if needed.
+// for int6, which carries a second code plane); one chunk per lane fits
+// any M tile except for 2-bit codes, whose 32 activation pairs per chunk and
+// row spill beyond an M tile of 4.  Shrinks the M tile if needed.
 bool gemv_plan(int k, int C, int* mt, int* KW, int* cpl) {
   const int kind = base_kind(k);
   const int budget = kind == K_AFF2 ? 4 : (kind == K_Q6K ? 4 : (kind == K_AFF8 ? 8 : 6));
+  const int mt_one_chunk = kind == K_AFF2 ? 4 : 8;
   for (int m = *mt; m >= 1; m /= 2) {
     for (int kw = 1; kw <= 4; kw *= 2) {
       int c = (C + 64 * kw - 1) / (64 * kw);
-      if (c <= 4 && (c * m <= budget || c == 1)) {
+      if (c <= 4 && (c * m <= budget || (c == 1 && m <= mt_one_chunk))) {
         *mt = m; *KW = kw; *cpl = c;
         return true;
       }
