@@ -275,13 +275,11 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
   if (kernel == QP_KERNEL_AUTO) {
     // The MFMA qGEMV dequantizes each weight once instead of doing one dot
     // product per activation row.  Where it takes over (measured on
-    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 3 for
-    // the fp16-dequantized int2/int4 affine and grouped SYM4, 6 for the
-    // fp32-dequantized int8 affine, Q4K and Q6K.
+    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 4 for
+    // Q6K (costly 6-bit dequantization), 3 for the others.
     int64_t mfma_from = 3;
     if (dd.fmt == qp::SYM4 && dd.gs == dd.K) mfma_from = 2;
-    else if (dd.fmt == qp::Q4K || dd.fmt == qp::Q6K || (dd.fmt == qp::AFFINE && dd.bits == 8))
-      mfma_from = 6;
+    else if (dd.fmt == qp::Q6K) mfma_from = 4;
     if (M >= mfma_from && M <= 16 && skinny_fits) use = USE_SKINNY;
     else if (M <= 8 && gemv_fits) use = USE_GEMV;
     else if (gemm_ok(dd)) use = USE_GEMM;
@@ -297,7 +295,8 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
     e = qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, (hipStream_t)stream);
     what = "qGEMM launch";
   } else if (use == USE_SKINNY) {
-    e = qp::launch_skinny(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, (hipStream_t)stream);
+    e = qp::launch_skinny(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, nbytes,
+                          (hipStream_t)stream);
     what = "MFMA qGEMV launch";
   } else {
     e = qp::launch_gemv(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, nbytes,

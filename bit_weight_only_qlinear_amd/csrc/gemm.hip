@@ -578,12 +578,15 @@ struct SkinnyArgs {
   void* y;
   int64_t M, N, K;
   int gs, ydt;
+  uint32_t meta_bytes[3];   // scales, zeros, steps: allocated sizes (16-byte multiples)
+  uint32_t lds_meta[3];     // LDS byte offsets of the staged metadata (LM kernels)
 };
 
 // One 128-column block of one lane: codes of its two rows (32 columns
 // each), their metadata, and its activation chunks.
 template <int KIND>
 struct SkStage {
+  int kb;                   // which column block
   uint4 x[4];
   uint32_t w[2][GT<KIND>::W / 2];
   uint32_t h[2][GT<KIND>::H > 0 ? GT<KIND>::H / 2 : 1];
@@ -661,9 +664,10 @@ struct SkRsrc {
   uint32_t g;                           // lane >> 4
 };
 
-template <int KIND, bool PERCH>
+template <int KIND, bool PERCH, bool LM>
 __device__ __forceinline__ void sk_load(const SkinnyArgs& a, const SkRsrc& r, int kb,
                                         SkStage<KIND>& st) {
+  st.kb = kb;
   const uint32_t c0 = (uint32_t)kb * kSkCols + 32u * r.g;   // lane's first column
   // activations: 32 columns = 64 bytes (rows past M read 0)
   const uint32_t xo = r.xo == 0xFFFFFFFFu ? 0x80000000u : r.xo + 2u * c0;
@@ -687,7 +691,13 @@ __device__ __forceinline__ void sk_load(const SkinnyArgs& a, const SkRsrc& r, in
       }
     }
     st.s0[i] = st.s1[i] = st.s2[i] = 0;
-    if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+    if constexpr (LM) {
+      if constexpr (KIND == G_Q6K) {   // the high plane is code data, not metadata
+        const uint2 v = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho[i] + c0 / 4u, 0, 0));
+        st.h[i][0] = v.x; st.h[i][1] = v.y;
+      }
+    } else if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
       const uint32_t g = c0 / (uint32_t)a.gs;
       st.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so[i] + 2u * g, 0, 0);
       st.s1[i] = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo[i] + 2u * g, 0, 0);
@@ -707,9 +717,42 @@ __device__ __forceinline__ void sk_load(const SkinnyArgs& a, const SkRsrc& r, in
   }
 }
 
-template <int KIND, bool XBF16, bool MBF16, bool PERCH>
+// Metadata of a stage's column block for the lane's two rows, from the
+// block's LDS copy (the same fields sk_load reads from HBM otherwise).
+template <int KIND, bool PERCH>
+__device__ __forceinline__ void sk_meta_lds(const SkinnyArgs& a, const unsigned char* smem,
+                                            int rr, uint32_t g4, SkStage<KIND>& st) {
+  const uint32_t c0 = (uint32_t)st.kb * kSkCols + 32u * g4;
+  const uint32_t K = (uint32_t)a.K;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t n = 16u * i + (uint32_t)rr;
+    if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
+      const uint32_t off = n * (K / (uint32_t)a.gs) * 2u + 2u * (c0 / (uint32_t)a.gs);
+      st.s0[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[0] + off);
+      st.s1[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[1] + off);
+    } else if constexpr (KIND == G_Q4K) {
+      st.s0[i] = smem[a.lds_meta[0] + n * (K / 32u) + c0 / 32u];
+      st.s1[i] = smem[a.lds_meta[1] + n * (K / 32u) + c0 / 32u];
+      st.s2[i] = *reinterpret_cast<const uint32_t*>(smem + a.lds_meta[2] + n * (K / 256u) * 4u +
+                                                    4u * (c0 / 256u));
+    } else if constexpr (KIND == G_Q6K) {
+      st.s0[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[0] + n * (K / 16u) + c0 / 16u);
+      st.s2[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[2] + n * (K / 256u) * 2u +
+                                                    2u * (c0 / 256u));
+    } else if constexpr (!PERCH) {
+      st.s0[i] = *reinterpret_cast<const uint32_t*>(smem + a.lds_meta[0] + n * (K / (uint32_t)a.gs) * 4u +
+                                                    4u * (c0 / (uint32_t)a.gs));
+    }
+  }
+}
+
+template <int KIND, bool XBF16, bool MBF16, bool PERCH, bool LM>
 __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
-  __shared__ float part[kSkWaves][2][16][17];   // per wave, tile, weight row, activation row
+  // LDS: partial sums [wave][tile][weight row][activation row] first, then
+  // (LM) the block's metadata rows
+  extern __shared__ __attribute__((aligned(16))) unsigned char sk_smem[];
+  float (*part)[2][16][17] = reinterpret_cast<float (*)[2][16][17]>(sk_smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -755,7 +798,8 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
   float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   const uint32_t magic = 0x64006400u;
 
-  auto compute = [&](const SkStage<KIND>& st) {
+  auto compute = [&](SkStage<KIND>& st) {
+    if constexpr (LM) sk_meta_lds<KIND, PERCH>(a, sk_smem, rr, r.g, st);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const half8_t B = __builtin_bit_cast(half8_t, act_chunk<XBF16>(st.x[t]));
@@ -774,15 +818,43 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
   const int J = wave < KB ? (KB - wave + kSkWaves - 1) / kSkWaves : 0;   // blocks of this wave
   static_for<kSkDepth>([&](auto P) {
     constexpr int p = decltype(P)::value;
-    if (p < J) sk_load<KIND, PERCH>(a, r, wave + p * kSkWaves, st[p]);
+    if (p < J) sk_load<KIND, PERCH, LM>(a, r, wave + p * kSkWaves, st[p]);
   });
+  if constexpr (LM) {
+    // copy the metadata rows [n0, n0 + 32) of every array into LDS in
+    // 16-byte units (rows are contiguous; the allocations are 16-byte
+    // multiples, so the rounded-up tail stays inside them)
+    const unsigned char* src[3] = {static_cast<const unsigned char*>(a.scales),
+                                   static_cast<const unsigned char*>(a.zeros),
+                                   static_cast<const unsigned char*>(a.steps)};
+    const uint32_t rowb[3] = {KIND == G_Q4K ? (uint32_t)(K / 32)
+                              : KIND == G_Q6K ? (uint32_t)(K / 16)
+                              : KIND == G_SYM4 ? (uint32_t)(K / a.gs) * 4u
+                                               : (uint32_t)(K / a.gs) * 2u,
+                              KIND == G_Q4K ? (uint32_t)(K / 32)
+                              : (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) ? (uint32_t)(K / a.gs) * 2u
+                                                                                     : 0u,
+                              KIND == G_Q4K ? (uint32_t)(K / 256) * 4u
+                              : KIND == G_Q6K ? (uint32_t)(K / 256) * 2u : 0u};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (rowb[q] == 0 || (PERCH && q == 0)) continue;
+      const uint64_t start = (uint64_t)n0 * rowb[q];
+      const auto rs = rsrc(src[q] + start, (uint32_t)(a.meta_bytes[q] - start));
+      const uint32_t units = ((uint32_t)nrows * rowb[q] + 15u) / 16u;
+      for (uint32_t u = (uint32_t)tid; u < units; u += 64u * kSkWaves)
+        *reinterpret_cast<uint4*>(sk_smem + a.lds_meta[q] + 16u * u) =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16u * u, 0, 0));
+    }
+    __syncthreads();
+  }
   for (int j0 = 0; j0 < J; j0 += R) {
     static_for<R>([&](auto Q) {
       constexpr int q = decltype(Q)::value;
       const int j = j0 + q;
       if (j < J) {
         if (j + kSkDepth < J)
-          sk_load<KIND, PERCH>(a, r, wave + (j + kSkDepth) * kSkWaves, st[(q + kSkDepth) % R]);
+          sk_load<KIND, PERCH, LM>(a, r, wave + (j + kSkDepth) * kSkWaves, st[(q + kSkDepth) % R]);
         compute(st[q]);
       }
     });
@@ -818,7 +890,8 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
 bool skinny_supported(const Desc& d) { return d.K % kSkCols == 0; }
 
 hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
-                         const void* bias, void* y, int ydt, hipStream_t s) {
+                         const void* bias, void* y, int ydt, const size_t bytes[5],
+                         hipStream_t s) {
   if (M < 1 || M > 16 || !skinny_supported(d)) return hipErrorInvalidValue;
   SkinnyArgs a;
   a.qw = b.qweight;
@@ -835,8 +908,26 @@ hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const
   a.gs = d.gs;
   a.ydt = ydt;
   const bool xb = xdt == BF16, mb = d.meta == BF16;
+  // metadata row bytes per array; staged in LDS when a block's rows fit
+  uint32_t rowb[3] = {0, 0, 0};
+  const uint32_t K = (uint32_t)d.K;
+  if (d.fmt == AFFINE) rowb[0] = rowb[1] = (K / d.gs) * 2u;
+  else if (d.fmt == Q4K) { rowb[0] = rowb[1] = K / 32u; rowb[2] = (K / 256u) * 4u; }
+  else if (d.fmt == Q6K) { rowb[0] = K / 16u; rowb[2] = (K / 256u) * 2u; }
+  else rowb[0] = (K / d.gs) * 4u;
+  uint32_t lds = (uint32_t)(sizeof(float) * kSkWaves * 2 * 16 * 17);
+  uint32_t metab = 0;
+  for (int q = 0; q < 3; ++q) {
+    a.meta_bytes[q] = (uint32_t)((bytes[2 + q] + 15) & ~size_t(15));
+    a.lds_meta[q] = lds + metab;
+    metab += (kSkRows * rowb[q] + 15u) & ~15u;
+  }
+  const bool lm = !(d.fmt == SYM4 && d.gs == d.K) && metab <= 64u * 1024u;
+  if (lm) lds += metab;
   void (*fn)(SkinnyArgs) = nullptr;
-#define QP_SK(KD, MB) fn = xb ? k_skinny<KD, true, MB, false> : k_skinny<KD, false, MB, false>;
+#define QP_SK(KD, MB) \
+  fn = lm ? (xb ? k_skinny<KD, true, MB, false, true> : k_skinny<KD, false, MB, false, true>) \
+          : (xb ? k_skinny<KD, true, MB, false, false> : k_skinny<KD, false, MB, false, false>);
   if (d.fmt == AFFINE) {
     if (d.bits == 2) { if (mb) { QP_SK(G_AFF2, true) } else { QP_SK(G_AFF2, false) } }
     else if (d.bits == 4) { if (mb) { QP_SK(G_AFF4, true) } else { QP_SK(G_AFF4, false) } }
@@ -846,13 +937,13 @@ hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const
   } else if (d.fmt == Q6K) {
     QP_SK(G_Q6K, false)
   } else if (d.gs == d.K) {
-    fn = xb ? k_skinny<G_SYM4, true, false, true> : k_skinny<G_SYM4, false, false, true>;
+    fn = xb ? k_skinny<G_SYM4, true, false, true, false> : k_skinny<G_SYM4, false, false, true, false>;
   } else {
     QP_SK(G_SYM4, false)
   }
 #undef QP_SK
   const unsigned blocks = (unsigned)((d.N + kSkRows - 1) / kSkRows);
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * kSkWaves), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * kSkWaves), lds, s, a);
   return hipGetLastError();
 }
 

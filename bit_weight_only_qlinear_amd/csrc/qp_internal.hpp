@@ -47,7 +47,7 @@ hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M,
 bool skinny_supported(const Desc& d);
 hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M,
                          const Bufs& b, const void* bias, void* y, int ydt,
-                         hipStream_t s);
+                         const size_t bytes[5], hipStream_t s);
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        hipStream_t s);
