@@ -221,7 +221,9 @@ __device__ __forceinline__ uint32_t field(const Stage<KIND>& st, int j, int e) {
 }
 
 // (t & m) | c in one instruction; m comes from an SGPR, c from a VGPR (one
-// VOP3 operand may be scalar).
+// VOP3 operand may be scalar).  Its result must pass through a compiler-
+// visible VALU instruction before an MFMA reads it: the hazard recognizer
+// does not see into inline asm.
 __device__ __forceinline__ uint32_t and_or(uint32_t t, uint32_t m, uint32_t c) {
   uint32_t r;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(t), "s"(m), "v"(c));
@@ -795,11 +797,42 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
   }
 
   typedef float float4_t __attribute__((ext_vector_type(4)));
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
   float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float4_t acc_c = {0.f, 0.f, 0.f, 0.f};
   const uint32_t magic = 0x64006400u;
+  // Per-channel SYM4 with bf16 activations runs on bf16 MFMA: the codes as
+  // bf16 are 128 + u exactly (0x4300 | u), the activations need only the
+  // column reorder, and one more MFMA per step with the constant -136 (the
+  // code offset 8 plus 128) accumulates -136 * sum(x) into acc_c, which is
+  // added to every tile at the end: sum (128 + u - 136) x = sum q x, exact
+  // products, fp32 accumulation.
+  constexpr bool BF = PERCH && XBF16;
+  const uint32_t magic_bf = 0x43004300u;
+  const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u,
+                                                                 0xC308C308u, 0xC308C308u));
 
   auto compute = [&](SkStage<KIND>& st) {
     if constexpr (LM) sk_meta_lds<KIND, PERCH>(a, sk_smem, rr, r.g, st);
+    if constexpr (BF) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, act_chunk<false>(st.x[t]));   // reorder only
+        acc_c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, B, acc_c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          uint32_t p[4];
+#pragma unroll
+          // plain C, not the inline-asm and_or: these values feed the MFMA
+          // directly, and only compiler-visible producers get the VALU-write
+          // -> MFMA-read wait states the hardware needs
+          for (int e = 0; e < 4; ++e) p[e] = ((st.w[i][t] >> (4 * e)) & 0x000F000Fu) | magic_bf;
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3])), B, acc[i], 0, 0, 0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const half8_t B = __builtin_bit_cast(half8_t, act_chunk<XBF16>(st.x[t]));
@@ -860,6 +893,10 @@ __global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
     });
   }
 
+  if constexpr (BF) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i] += acc_c;
+  }
   // ---- partial sums of the 8 waves meet in LDS
 #pragma unroll
   for (int i = 0; i < 2; ++i)
