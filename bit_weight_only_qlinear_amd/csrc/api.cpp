@@ -280,7 +280,11 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
     int64_t mfma_from = 3;
     if (dd.fmt == qp::SYM4 && dd.gs == dd.K) mfma_from = 2;
     else if (dd.fmt == qp::Q6K) mfma_from = 4;
-    if (M >= mfma_from && M <= 16 && skinny_fits) use = USE_SKINNY;
+    // fp16-rounded weights add an error that grows like sqrt(K) against the
+    // layer's element bound; past K = 16384 small M stays on the exact-code
+    // qGEMV
+    const bool exact_preferred = dd.K > 16384 && M <= 8 && gemv_fits;
+    if (M >= mfma_from && M <= 16 && skinny_fits && !exact_preferred) use = USE_SKINNY;
     else if (M <= 8 && gemv_fits) use = USE_GEMV;
     else if (gemm_ok(dd)) use = USE_GEMM;
     else if (gemv_fits) use = USE_GEMV;

@@ -115,8 +115,8 @@ typedef enum { QP_F16 = 0, QP_BF16 = 1, QP_F32 = 2 } qp_dtype;
 typedef enum {
   QP_KERNEL_AUTO = 0,      /* small M: qGEMV; from M = 2 (per-channel SYM4),
                               4 (Q6K) or 3 (other formats) up to M = 16: MFMA
-                              qGEMV when K % 128 == 0 (else qGEMV up to
-                              M = 8); larger M: qGEMM                        */
+                              qGEMV when K % 128 == 0 and K <= 16384 (else
+                              qGEMV up to M = 8); larger M: qGEMM            */
   QP_KERNEL_GEMV = 1,      /* decode-shaped kernel, any M (processed 8 at once) */
   QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M               */
   QP_KERNEL_GEMV_MFMA = 3  /* decode-shaped MFMA kernel, M <= 16, K % 128 == 0 */

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from bit_weight_only_qlinear_amd import synth
-from helpers import (qformat_of, to_dev_bits, oracle_buffers, gpu_rows, check_linear,
+from helpers import (f16_weight_bound, qformat_of, to_dev_bits, oracle_buffers, gpu_rows, check_linear,
                      buf_to_np, y_to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -120,7 +120,7 @@ def test_quantize_exhaustive_codes_roundtrip(q):
 
 
 # --------------------------------------------------------------- forward
-def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None):
+def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_weights=False):
     W = _weights(d.N, d.K, seed)
     rng = np.random.default_rng(seed + 1)
     xb = synth.draw_activations(rng, M, d.K, xdtype)
@@ -136,7 +136,8 @@ def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None):
     w64 = oracle.dequant_f64(qz, f)
     b64 = oracle.decode_activations(bias_bits, xdtype) if with_bias else None
     y_ref = oracle.linear_f64(x64, qz, f, b64, w64=w64)
-    return check_linear(y, y_ref, x64, np.abs(w64).max(), d.K, ydt)
+    extra = f16_weight_bound(x64, w64) if f16_weights else None
+    return check_linear(y, y_ref, x64, np.abs(w64).max(), d.K, ydt, extra=extra)
 
 
 GEMV_SHAPES = [(1, 256), (3, 512), (77, 1024), (300, 4096), (513, 5120), (64, 8192)]
@@ -163,6 +164,25 @@ def test_gemv_mfma_forward(q, N, K, M):
             print("gemv_mfma", _id(d), M, xdt, ydt, flush=True)
             _forward_case(q, d, M, xdt, ydt, q.QP_KERNEL_GEMV_MFMA, seed=N * 37 + K + M + i,
                           with_bias=(i % 2 == 1))
+
+
+@pytest.mark.parametrize("fmt", ["affine32", "q4k", "q6k", "sym4g32"])
+def test_gemv_mfma_large_k(q, fmt):
+    """K = 32768: a block's metadata no longer fits LDS, so the MFMA qGEMV
+    reads it per step from HBM (the other code path of the kernel).  At this
+    K the fp16 rounding of the weights can exceed the layer's element bound,
+    so the MFMA kernels are held to it plus the fp16-weight bound.  The
+    exact-code qGEMV's register plan stops short of this K, so AUTO picks an
+    fp16-weight kernel here as well."""
+    N, K = 40, 32768
+    d = {"affine32": q.QDesc.affine(N, K, 4, 32, "bf16"), "q4k": q.QDesc.q4k(N, K),
+         "q6k": q.QDesc.q6k(N, K), "sym4g32": q.QDesc.sym4(N, K, 32)}[fmt]
+    for M in (4, 9):
+        print("gemv_mfma large K", _id(d), M, flush=True)
+        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMV_MFMA, seed=M + 7, with_bias=True,
+                      f16_weights=True)
+        _forward_case(q, d, M, "bf16", "bf16", q.QP_KERNEL_AUTO, seed=M + 8, with_bias=False,
+                      f16_weights=True)
 
 
 @pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768)])
