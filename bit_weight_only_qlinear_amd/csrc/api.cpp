@@ -160,7 +160,9 @@ qp_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-bool gemm_ok(const qp::Desc& d) { return d.K % 64 == 0; }
+// The qGEMM addresses a block's 256 activation rows through a 32-bit buffer
+// resource (256 * K * 2 bytes), hence K <= 2^22.
+bool gemm_ok(const qp::Desc& d) { return d.K % 64 == 0 && d.K <= (int64_t(1) << 22); }
 
 }  // namespace
 
@@ -255,21 +257,22 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
       kernel != QP_KERNEL_GEMV_MFMA)
     return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
   if (kernel == QP_KERNEL_GEMM && !gemm_ok(dd))
-    return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 (K=%lld)", (long long)dd.K);
+    return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 and K <= 2^22 (K=%lld)",
+                (long long)dd.K);
   size_t nbytes[5];
   sizes_of(dd, nbytes);
   bool small_bufs = (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
   for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
   const bool gemv_fits = qp::gemv_supported(dd) && small_bufs;
-  const bool skinny_fits = qp::skinny_supported(dd) && M <= 16 &&
-                           (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
+  const bool skinny_fits = qp::skinny_supported(dd) && M <= 16 && small_bufs;
   if (kernel == QP_KERNEL_GEMV && !gemv_fits)
     return fail(QP_EUNSUPPORTED,
                 "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
                 (long long)dd.K);
   if (kernel == QP_KERNEL_GEMV_MFMA && !skinny_fits)
     return fail(QP_EUNSUPPORTED,
-                "the MFMA qGEMV kernel needs M <= 16 and K %% 128 == 0 (M=%lld, K=%lld)",
+                "the MFMA qGEMV kernel needs M <= 16, K %% 128 == 0 and every buffer < 2 GiB "
+                "(M=%lld, K=%lld)",
                 (long long)M, (long long)dd.K);
   enum { USE_GEMV, USE_SKINNY, USE_GEMM } use;
   if (kernel == QP_KERNEL_AUTO) {

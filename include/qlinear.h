@@ -118,8 +118,10 @@ typedef enum {
                               qGEMV when K % 128 == 0 and K <= 16384 (else
                               qGEMV up to M = 8); larger M: qGEMM            */
   QP_KERNEL_GEMV = 1,      /* decode-shaped kernel, any M (processed 8 at once) */
-  QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M               */
-  QP_KERNEL_GEMV_MFMA = 3  /* decode-shaped MFMA kernel, M <= 16, K % 128 == 0 */
+  QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M; K % 64 == 0,
+                              K <= 2^22                                      */
+  QP_KERNEL_GEMV_MFMA = 3  /* decode-shaped MFMA kernel, M <= 16, K % 128 == 0,
+                              every buffer < 2 GiB                           */
 } qp_kernel;
 
 typedef struct {

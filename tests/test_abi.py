@@ -112,8 +112,10 @@ def test_forward_argument_validation(q):
     assert _call_forward(q, q.QDesc.q4k(64, 512), w=w) == q.QP_EINVAL and "steps" in _err(q)
     w = q._Weights(FAKE, None, FAKE, None, FAKE)
     assert _call_forward(q, q.QDesc.q6k(64, 512), w=w) == q.QP_EINVAL and "qweight_hi" in _err(q)
-    # the MFMA kernel needs K % 64 == 0
+    # the MFMA kernel needs K % 64 == 0 and K <= 2^22
     assert _call_forward(q, q.QDesc.affine(8, 96, 4, 32), kernel=2) == q.QP_EUNSUPPORTED
+    assert _call_forward(q, q.QDesc.affine(8, 1 << 23, 4, 64), M=64,
+                         kernel=2) == q.QP_EUNSUPPORTED and "2^22" in _err(q)
     # the MFMA qGEMV needs K % 128 == 0 and M <= 16
     assert _call_forward(q, q.QDesc.affine(8, 192, 4, 64), M=4,
                          kernel=q.QP_KERNEL_GEMV_MFMA) == q.QP_EUNSUPPORTED
