@@ -90,11 +90,17 @@ KERNEL_SOURCES = ("gemv.hip", "device_common.hpp", "qp_internal.hpp")
 
 
 def kernel_source_hash():
+    """First 16 hex digits of the SHA-256 of the kernel sources with comments
+    and whitespace removed: the counters stay valid across comment edits."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_weight_only_qlinear_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "bit_weight_only_qlinear_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,8 +13,11 @@
 //    per-lane metadata loads interleaved with the code stream cost more than
 //    half of HBM bandwidth; the staged copy keeps the HBM traffic in long
 //    contiguous runs.
-//  * Activations.  The lane's slice of x is loaded once, rearranged into the
-//    bf16 (fp16) pairs that match the code pairs, and reused for every row.
+//  * Activations.  With one activation row the block stages x in LDS next to
+//    the metadata; each lane takes its slice from there (SYM4: the block
+//    builds the pairs once), rearranged into the bf16 (fp16) pairs that
+//    match the code pairs, and reuses it for every row.  With several rows
+//    (M tile > 1) each lane loads its slices directly.
 //  * Arithmetic.  Codes become bf16 (fp16) pairs without a conversion
 //    instruction: v_perm_b32 places a code byte under the high byte of 128.0
 //    bf16 (1024.0 fp16), which is exactly 128 + q (1024 + q).  One v_dot2
