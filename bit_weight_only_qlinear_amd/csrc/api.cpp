@@ -235,17 +235,92 @@ qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out, i
                     "qpack_dequantize launch");
 }
 
-qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
-                                 const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
-                                 int32_t kernel, void* stream) {
-  qp::Desc dd;
-  qp_status st = check_desc(d, &dd);
+}  // extern "C"
+
+namespace {
+
+enum Use { USE_GEMV, USE_SKINNY, USE_GEMM };
+
+// Checks the forward arguments that do not involve a workspace and picks the
+// kernel family.
+qp_status plan_forward(const qp_desc* d, qp::Desc* dd, int32_t x_dtype, int64_t M,
+                       int32_t kernel, Use* use, size_t nbytes[5]) {
+  qp_status st = check_desc(d, dd);
   if (st != QP_OK) return st;
-  if ((st = check_weights(dd, w, false)) != QP_OK) return st;
   if (M <= 0) return fail(QP_ESHAPE, "M must be positive (got %lld)", (long long)M);
   if (M > (int64_t(1) << 24)) return fail(QP_EUNSUPPORTED, "M must be <= 2^24");
   if (x_dtype != QP_F16 && x_dtype != QP_BF16)
     return fail(QP_EINVAL, "x_dtype must be QP_F16 or QP_BF16 (got %d)", x_dtype);
+  if (kernel != QP_KERNEL_AUTO && kernel != QP_KERNEL_GEMV && kernel != QP_KERNEL_GEMM &&
+      kernel != QP_KERNEL_GEMV_MFMA)
+    return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
+  if (kernel == QP_KERNEL_GEMM && !gemm_ok(*dd))
+    return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 and K <= 2^22 (K=%lld)",
+                (long long)dd->K);
+  sizes_of(*dd, nbytes);
+  bool small_bufs = (size_t)M * (size_t)dd->K * 2 < (size_t(1) << 31);
+  for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
+  const bool gemv_fits = qp::gemv_supported(*dd) && small_bufs;
+  const bool skinny_fits = qp::skinny_supported(*dd) && M <= 16 && small_bufs;
+  if (kernel == QP_KERNEL_GEMV && !gemv_fits)
+    return fail(QP_EUNSUPPORTED,
+                "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
+                (long long)dd->K);
+  if (kernel == QP_KERNEL_GEMV_MFMA && !skinny_fits)
+    return fail(QP_EUNSUPPORTED,
+                "the MFMA qGEMV kernel needs M <= 16, K %% 128 == 0 and every buffer < 2 GiB "
+                "(M=%lld, K=%lld)",
+                (long long)M, (long long)dd->K);
+  if (kernel == QP_KERNEL_AUTO) {
+    // The MFMA qGEMV dequantizes each weight once instead of doing one dot
+    // product per activation row.  Where it takes over (measured on
+    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 4 for
+    // Q6K (costly 6-bit dequantization), 3 for the others.
+    int64_t mfma_from = 3;
+    if (dd->fmt == qp::SYM4 && dd->gs == dd->K) mfma_from = 2;
+    else if (dd->fmt == qp::Q6K) mfma_from = 4;
+    // fp16-rounded weights add an error that grows like sqrt(K) against the
+    // layer's element bound; past K = 16384 small M stays on the exact-code
+    // qGEMV
+    const bool exact_preferred = dd->K > 16384 && M <= 8 && gemv_fits;
+    if (M >= mfma_from && M <= 16 && skinny_fits && !exact_preferred) *use = USE_SKINNY;
+    else if (M <= 8 && gemv_fits) *use = USE_GEMV;
+    else if (gemm_ok(*dd)) *use = USE_GEMM;
+    else if (gemv_fits) *use = USE_GEMV;
+    else return fail(QP_EUNSUPPORTED, "no kernel supports K=%lld for this format", (long long)dd->K);
+  } else {
+    *use = kernel == QP_KERNEL_GEMM ? USE_GEMM : kernel == QP_KERNEL_GEMV_MFMA ? USE_SKINNY : USE_GEMV;
+  }
+  return QP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qp_status qlinear_workspace_bytes(const qp_desc* d, int32_t x_dtype, int64_t M, int32_t kernel,
+                                  size_t* bytes) {
+  if (!bytes) return fail(QP_EINVAL, "bytes is NULL");
+  *bytes = 0;
+  qp::Desc dd;
+  Use use;
+  size_t nbytes[5];
+  qp_status st = plan_forward(d, &dd, x_dtype, M, kernel, &use, nbytes);
+  if (st != QP_OK) return st;
+  if (use == USE_GEMM) *bytes = qp::gemm_workspace_bytes(dd, M);
+  return ok();
+}
+
+qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
+                             const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
+                             int32_t kernel, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  qp::Desc dd;
+  Use use;
+  size_t nbytes[5];
+  qp_status st = plan_forward(d, &dd, x_dtype, M, kernel, &use, nbytes);
+  if (st != QP_OK) return st;
+  if ((st = check_weights(dd, w, false)) != QP_OK) return st;
   if (y_dtype != QP_F16 && y_dtype != QP_BF16 && y_dtype != QP_F32)
     return fail(QP_EINVAL, "y_dtype must be QP_F16, QP_BF16 or QP_F32 (got %d)", y_dtype);
   if (!x) return fail(QP_EINVAL, "x is NULL");
@@ -253,53 +328,23 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
   if (!aligned16(x)) return fail(QP_EALIGN, "x is not 16-byte aligned");
   if (!aligned16(y)) return fail(QP_EALIGN, "y is not 16-byte aligned");
   if (bias && !aligned16(bias)) return fail(QP_EALIGN, "bias is not 16-byte aligned");
-  if (kernel != QP_KERNEL_AUTO && kernel != QP_KERNEL_GEMV && kernel != QP_KERNEL_GEMM &&
-      kernel != QP_KERNEL_GEMV_MFMA)
-    return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
-  if (kernel == QP_KERNEL_GEMM && !gemm_ok(dd))
-    return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 and K <= 2^22 (K=%lld)",
-                (long long)dd.K);
-  size_t nbytes[5];
-  sizes_of(dd, nbytes);
-  bool small_bufs = (size_t)M * (size_t)dd.K * 2 < (size_t(1) << 31);
-  for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
-  const bool gemv_fits = qp::gemv_supported(dd) && small_bufs;
-  const bool skinny_fits = qp::skinny_supported(dd) && M <= 16 && small_bufs;
-  if (kernel == QP_KERNEL_GEMV && !gemv_fits)
-    return fail(QP_EUNSUPPORTED,
-                "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
-                (long long)dd.K);
-  if (kernel == QP_KERNEL_GEMV_MFMA && !skinny_fits)
-    return fail(QP_EUNSUPPORTED,
-                "the MFMA qGEMV kernel needs M <= 16, K %% 128 == 0 and every buffer < 2 GiB "
-                "(M=%lld, K=%lld)",
-                (long long)M, (long long)dd.K);
-  enum { USE_GEMV, USE_SKINNY, USE_GEMM } use;
-  if (kernel == QP_KERNEL_AUTO) {
-    // The MFMA qGEMV dequantizes each weight once instead of doing one dot
-    // product per activation row.  Where it takes over (measured on
-    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 4 for
-    // Q6K (costly 6-bit dequantization), 3 for the others.
-    int64_t mfma_from = 3;
-    if (dd.fmt == qp::SYM4 && dd.gs == dd.K) mfma_from = 2;
-    else if (dd.fmt == qp::Q6K) mfma_from = 4;
-    // fp16-rounded weights add an error that grows like sqrt(K) against the
-    // layer's element bound; past K = 16384 small M stays on the exact-code
-    // qGEMV
-    const bool exact_preferred = dd.K > 16384 && M <= 8 && gemv_fits;
-    if (M >= mfma_from && M <= 16 && skinny_fits && !exact_preferred) use = USE_SKINNY;
-    else if (M <= 8 && gemv_fits) use = USE_GEMV;
-    else if (gemm_ok(dd)) use = USE_GEMM;
-    else if (gemv_fits) use = USE_GEMV;
-    else return fail(QP_EUNSUPPORTED, "no kernel supports K=%lld for this format", (long long)dd.K);
-  } else {
-    use = kernel == QP_KERNEL_GEMM ? USE_GEMM : kernel == QP_KERNEL_GEMV_MFMA ? USE_SKINNY : USE_GEMV;
+  if (workspace && !aligned16(workspace))
+    return fail(QP_EALIGN, "workspace is not 16-byte aligned");
+  void* ws = nullptr;
+  if (use == USE_GEMM && workspace) {
+    const size_t need = qp::gemm_workspace_bytes(dd, M);
+    if (need > 0) {
+      if (workspace_bytes < need)
+        return fail(QP_EINVAL, "workspace too small: %zu bytes, this call needs %zu",
+                    workspace_bytes, need);
+      ws = workspace;
+    }
   }
   (void)hipGetLastError();
   hipError_t e;
   const char* what;
   if (use == USE_GEMM) {
-    e = qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, (hipStream_t)stream);
+    e = qp::launch_gemm(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, ws, (hipStream_t)stream);
     what = "qGEMM launch";
   } else if (use == USE_SKINNY) {
     e = qp::launch_skinny(dd, x, x_dtype, M, bufs_of(w), bias, y, y_dtype, nbytes,
@@ -311,6 +356,12 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
     what = "qGEMV launch";
   }
   return hip_status(e, what);
+}
+
+qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
+                                 const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
+                                 int32_t kernel, void* stream) {
+  return qlinear_forward_ws(d, x, x_dtype, M, w, bias, y, y_dtype, kernel, nullptr, 0, stream);
 }
 
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,

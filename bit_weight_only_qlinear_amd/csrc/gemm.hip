@@ -91,6 +91,7 @@ struct GemmArgs {
   const void* zeros;
   const void* steps;
   const void* x;
+  const void* xf;   // activations staged by k_xprep (k_gemm224), else null
   const void* bias;
   void* y;
   int64_t M, N, K;
@@ -142,14 +143,16 @@ struct Rsrc {
 // Every offset is a per-lane (voffset) offset, so the buffer range check
 // covers all of it: steps at or past K (the pipeline's two phantom steps)
 // read either the next row's data or 0, never memory outside the buffers.
-template <int KIND, bool GS32>
+template <int KIND, bool GS32, bool LOADX = true>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int kt,
                                            Stage<KIND>& st) {
-  const uint32_t xk = (uint32_t)kt * (BK * 2);
+  if constexpr (LOADX) {
+    const uint32_t xk = (uint32_t)kt * (BK * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    st.x[i] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, r.xo + (uint32_t)i * r.xstride + xk, 0, 0));
+    for (int i = 0; i < 4; ++i)
+      st.x[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, r.xo + (uint32_t)i * r.xstride + xk, 0, 0));
+  }
   constexpr int W = GT<KIND>::W;
   const uint32_t wk = r.wo + (uint32_t)kt * (W * 4);
   if constexpr (W == 4) {
@@ -305,6 +308,42 @@ __device__ __forceinline__ void convert_part(const Stage<KIND>& st, int p, unsig
   *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16>(st, p, magic);
 }
 
+// Weight-side buffer resources and offsets of a block's rows n0 .. n0 +
+// nrows - 1 (rows past them read 0); thread t stages half row wrow_of(t).
+template <int KIND>
+__device__ __forceinline__ void weight_rsrc(const GemmArgs& a, int64_t n0, int64_t nrows, int tid,
+                                            Rsrc& r) {
+  const int64_t K = a.K;
+  const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
+  r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
+  r.half = (uint32_t)(tid & 1);
+  const int64_t n = wrow_of(tid);
+  r.wo = (uint32_t)(n * wrow) + r.half * (uint32_t)(GT<KIND>::W * 2);
+  r.h = r.w;
+  r.ho = 0;
+  if constexpr (KIND == G_Q6K) {
+    r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
+    r.ho = (uint32_t)(n * (K / 4)) + r.half * 8u;
+  }
+  int64_t srow = 0, zrow = 0, prow = 0;   // bytes per weight row
+  if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
+  else if constexpr (KIND == G_Q6K) { srow = K / 16; prow = (K / 256) * 2; }
+  else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
+  else { srow = (K / a.gs) * 2; zrow = srow; }
+  r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
+  r.so = (uint32_t)(n * srow);
+  r.z = r.s; r.zo = r.so;
+  if (zrow) {
+    r.z = rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow));
+    r.zo = (uint32_t)(n * zrow);
+  }
+  r.p = r.s; r.po = 0;
+  if (prow) {
+    r.p = rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow));
+    r.po = (uint32_t)(n * prow);
+  }
+}
+
 template <int KIND, bool XBF16, bool MBF16, bool GS32>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs a) {
@@ -333,34 +372,7 @@ k_gemm(GemmArgs a) {
     r.x = rsrc(static_cast<const unsigned char*>(a.x) + m0 * K * 2, (uint32_t)mrows * xrow);
     r.xo = (uint32_t)(tid >> 3) * xrow + (uint32_t)(tid & 7) * 16u;
     r.xstride = 64u * xrow;
-    const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
-    r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
-    r.half = (uint32_t)(tid & 1);
-    const int64_t n = wrow_of(tid);
-    r.wo = (uint32_t)(n * wrow) + r.half * (uint32_t)(GT<KIND>::W * 2);
-    r.h = r.w;
-    r.ho = 0;
-    if constexpr (KIND == G_Q6K) {
-      r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
-      r.ho = (uint32_t)(n * (K / 4)) + r.half * 8u;
-    }
-    int64_t srow = 0, zrow = 0, prow = 0;   // bytes per weight row
-    if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
-    else if constexpr (KIND == G_Q6K) { srow = K / 16; prow = (K / 256) * 2; }
-    else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
-    else { srow = (K / a.gs) * 2; zrow = srow; }
-    r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
-    r.so = (uint32_t)(n * srow);
-    r.z = r.s; r.zo = r.so;
-    if (zrow) {
-      r.z = rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow));
-      r.zo = (uint32_t)(n * zrow);
-    }
-    r.p = r.s; r.po = 0;
-    if (prow) {
-      r.p = rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow));
-      r.po = (uint32_t)(n * prow);
-    }
+    weight_rsrc<KIND>(a, n0, nrows, tid, r);
   }
 
   float16_t acc[4][2];
@@ -537,6 +549,214 @@ k_gemm(GemmArgs a) {
           }
         }
       });
+    });
+  });
+}
+
+// ===========================================================================
+// qGEMM with 224-row weight tiles and staged activations (k_gemm224).
+//
+// Where N is 7 * 2^k (14336 = 7 * 2048), 256 x 256 tiles leave the last
+// wave of blocks partly empty: at M = 2048 they make 448 blocks, 1.75 waves
+// on 256 CUs.  224 (n) x 256 (m) tiles make 512 blocks, two full waves of
+// 7/8 the work each.  A wave then owns 112 weight rows, not a multiple of
+// 32, so this kernel runs v_mfma_f32_16x16x32_f16: 7 x 4 tiles of 16 x 16
+// per wave (wave grid 2 (n) x 4 (m) as in k_gemm).  The activations are
+// staged once per call by k_xprep as fp16 in that MFMA's B-fragment order,
+// and each wave loads its B fragments straight into registers, one step
+// ahead; only the weight tile goes through LDS, staged, swizzled and
+// dequantized as in k_gemm (rows 224..255 of the LDS tile are unused).
+// ===========================================================================
+constexpr int BN7 = 224;
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Stages x [M, K] (bf16 or fp16) for k_gemm224: fp16 in the B-fragment order
+// of v_mfma_f32_16x16x32_f16.  16-byte chunk c = (mb * K/32 + kq) * 64 + l
+// holds row 16 mb + (l & 15), columns 32 kq + 8 (l >> 4) .. + 7 in the order
+// (0,4,1,5,2,6,3,7); rows from M up to the next multiple of 16 are zero.
+template <bool XBF16>
+__global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
+                                               uint4* __restrict__ xf, uint32_t M, uint32_t K,
+                                               uint32_t nchunks) {
+  const uint32_t c = blockIdx.x * 256u + threadIdx.x;
+  if (c >= nchunks) return;
+  const uint32_t l = c & 63u, blk = c >> 6, kb = K / 32u;
+  const uint32_t mb = blk / kb, kq = blk - mb * kb;
+  const uint32_t row = 16u * mb + (l & 15u), col = 32u * kq + 8u * (l >> 4);
+  uint4 u = make_uint4(0u, 0u, 0u, 0u);
+  if (row < M) u = *reinterpret_cast<const uint4*>(x + (uint64_t)row * K + col);
+  xf[c] = act_chunk<XBF16>(u);
+}
+
+template <int KIND, bool XBF16, bool MBF16, bool GS32>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+k_gemm224(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 2, wj = wave & 3;   // n half (112 rows), m quarter (64 rows)
+
+  const int T = a.tilesM * a.tilesN;
+  const int bid = blockIdx.x;
+  const int tile = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;  // as in k_gemm
+  const int tm = tile % a.tilesM, tn = tile / a.tilesM;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN7;
+  const int64_t nrows = a.N - n0 < BN7 ? a.N - n0 : BN7;
+  const int64_t K = a.K;
+
+  Rsrc r;
+  weight_rsrc<KIND>(a, n0, nrows, tid, r);
+  // staged activations of rows m0 .. m0 + 255 (M rounded up to 16 is staged)
+  const int64_t srows = (a.M + 15) / 16 * 16 - m0;
+  const __amdgpu_buffer_rsrc_t xr = rsrc(static_cast<const unsigned char*>(a.xf) + m0 * K * 2,
+                                         (uint32_t)((srows < BM ? srows : BM) * K * 2));
+  const uint32_t xfj = (uint32_t)(K * 32);   // 16 rows
+  const uint32_t xfo = (uint32_t)(4 * wj) * xfj + (uint32_t)lane * 16u;
+
+  float4_t acc[7][4];
+#pragma unroll
+  for (int i = 0; i < 7; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // A fragment (weight rows): lane row wi*112 + 16 i + (lane & 15), 16-byte
+  // chunk 4 sub + (lane >> 4), stored at chunk ^ ((row >> 1) & 7), and
+  // (row >> 1) & 7 == ((lane & 15) >> 1) since 112 and 16 are multiples of 16
+  uint32_t fa[2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+    fa[sub] = (uint32_t)(wi * 112 + (lane & 15)) * 128u +
+              (uint32_t)(((4 * sub + (lane >> 4)) ^ ((lane & 15) >> 1)) * 16);
+  auto rd_a = [&](uint32_t buf, int sub, int i) {
+    return *reinterpret_cast<const half8_t*>(smem + fa[sub] + (buf * kTileBytes + 2048u * i));
+  };
+  // B fragment (j, sub) of step kt: one contiguous 1 KiB wave load
+  auto ld_b = [&](int kt, int sub, int j) {
+    return __builtin_bit_cast(
+        half8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                     xr, xfo + (uint32_t)j * xfj + (uint32_t)(2 * kt + sub) * 1024u, 0, 0));
+  };
+  // weight chunk p of thread's half row into LDS stage buffer buf
+  const int wn = wrow_of(tid);
+  auto st_w = [&](uint32_t buf, int p, uint4 v) {
+    const int j = 4 * (tid & 1) + p;
+    const uint32_t wb = (uint32_t)wn * 128u + (uint32_t)((j ^ ((wn >> 1) & 7)) * 16);
+    *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = v;
+  };
+
+  const int KT = (int)(K / BK);
+  const uint32_t magic = 0x64006400u;
+  half8_t Bf[2][4];
+
+  // One k-step (two MFMA k-substeps of 32): MFMAs on LDS buffer kt & 1 and
+  // the B fragments of step kt; dequantization of the registers of step
+  // kt + 1 (`nxt`) into the other buffer; weight loads of step kt + 2 into
+  // `fre` and B fragment loads of step kt + 1.  Phantom steps at the end
+  // stay inside the buffers (range-checked offsets), as in k_gemm.
+  // Instruction order is pinned with scheduling fences.
+  auto kstep = [&](int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
+    const uint32_t cur = (uint32_t)(kt & 1);
+    load_stage<KIND, GS32, false>(a, r, kt + 2, fre);
+    __builtin_amdgcn_sched_barrier(0);
+    half8_t A[7];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) A[i] = rd_a(cur, 0, i);
+    static_for<2>([&](auto SUB) {
+      constexpr int sub = decltype(SUB)::value;
+      half8_t An[7];
+      if constexpr (sub == 0) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) An[i] = rd_a(cur, 1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const uint4 w0 = weight_chunk<KIND, MBF16>(nxt, 2 * sub, magic);
+      const uint4 w1 = weight_chunk<KIND, MBF16>(nxt, 2 * sub + 1, magic);
+      static_for<7>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        static_for<4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], Bf[sub][j], acc[i][j], 0, 0, 0);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(kt + 1, sub, j);
+      st_w(cur ^ 1u, 2 * sub, w0);
+      st_w(cur ^ 1u, 2 * sub + 1, w1);
+      if constexpr (sub == 0) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) A[i] = An[i];
+      }
+    });
+    __syncthreads();
+  };
+
+  Stage<KIND> st0, st1;
+  load_stage<KIND, GS32, false>(a, r, 0, st0);
+  load_stage<KIND, GS32, false>(a, r, 1, st1);
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(0, sub, j);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) st_w(0u, p, weight_chunk<KIND, MBF16>(st0, p, magic));
+  __syncthreads();
+  for (int kt = 0; kt < KT; kt += 2) {
+    kstep(kt, st0, st1);
+    if (kt + 1 < KT) kstep(kt + 1, st1, st0);
+  }
+
+  // ---- epilogue: lane holds rows n = 16 i + 4 (lane >> 4) + v (v = 0..3)
+  // of column m = 16 j + (lane & 15) of the wave's tiles.
+  const bool vec4 = (a.N % 4) == 0;
+  const int ydt = a.ydt;
+  const uint16_t* bias = static_cast<const uint16_t*>(a.bias);
+  int el = lane;
+  asm volatile("" : "+v"(el));   // keeps the epilogue's addresses after the loop
+  static_for<7>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int64_t n = n0 + wi * 112 + i * 16 + 4 * (el >> 4);
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t nn = n + v < a.N ? n + v : a.N - 1;
+        const uint32_t bb = bias[nn];
+        bv[v] = XBF16 ? bf16_to_f32(bb) : f16_to_f32(bb);   // bias has the x dtype
+      }
+    }
+    static_for<4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int64_t m = m0 + wj * 64 + j * 16 + (el & 15);
+      const int64_t idx = m * a.N + n;
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+      const bool mok = m < a.M;
+      if (mok && vec4 && n < a.N) {
+        if (ydt == F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.y) + idx) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          uint32_t h[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            h[q] = ydt == BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + idx) =
+              make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        }
+      } else if (mok && !vec4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (n + q < a.N) {
+            if (ydt == F32) static_cast<float*>(a.y)[idx + q] = v[q];
+            else static_cast<uint16_t*>(a.y)[idx + q] =
+                (uint16_t)(ydt == BF16 ? f32_to_bf16_rne(v[q]) : f32_to_f16_rne(v[q]));
+          }
+        }
+      }
     });
   });
 }
@@ -984,8 +1204,44 @@ hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const
   return hipGetLastError();
 }
 
+namespace {
+
+constexpr int64_t kCUs = 256;   // MI355X compute units
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 224-row tiles when they need less time than 256-row tiles counted in
+// waves of blocks over the CUs (one block per CU at a time).
+bool use_n224(const Desc& d, int64_t M) {
+  const int64_t tm = cdiv(M, BM);
+  return cdiv(tm * cdiv(d.N, BN7), kCUs) * BN7 < cdiv(tm * cdiv(d.N, BN), kCUs) * BN;
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(const Desc& d, int64_t M) {
+  if (!use_n224(d, M)) return 0;
+  const uint64_t bytes = (uint64_t)cdiv(M, 16) * 16u * (uint64_t)d.K * 2u;
+  // 32-bit chunk indices in k_xprep and 32-bit buffer offsets
+  return bytes <= (uint64_t(1) << 31) ? (size_t)bytes : 0;
+}
+
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
-                       const void* bias, void* y, int ydt, hipStream_t s) {
+                       const void* bias, void* y, int ydt, void* ws, hipStream_t s) {
+  const size_t wsb = ws ? gemm_workspace_bytes(d, M) : 0;
+  const bool n224 = wsb > 0;
+  if (n224) {
+    const uint32_t nchunks = (uint32_t)(wsb / 16u);
+    const unsigned xblocks = (nchunks + 255u) / 256u;
+    if (xdt == BF16)
+      hipLaunchKernelGGL(k_xprep<true>, dim3(xblocks), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
+                         (uint32_t)d.K, nchunks);
+    else
+      hipLaunchKernelGGL(k_xprep<false>, dim3(xblocks), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
+                         (uint32_t)d.K, nchunks);
+  }
   GemmArgs a;
   a.qw = b.qweight;
   a.qh = b.qweight_hi;
@@ -993,6 +1249,7 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.zeros = b.zeros;
   a.steps = b.steps;
   a.x = x;
+  a.xf = n224 ? ws : nullptr;
   a.bias = bias;
   a.y = y;
   a.M = M;
@@ -1001,13 +1258,14 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.gs = d.gs;
   a.ydt = ydt;
   a.tilesM = (int)((M + BM - 1) / BM);
-  a.tilesN = (int)((d.N + BN - 1) / BN);
+  a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
   void (*fn)(GemmArgs) = nullptr;
   // (kind, x dtype, metadata dtype, two groups per 64-column step)
 #define QP_GEMM_FLAGS(KD, MB, G)                                                 \
-  fn = xb ? k_gemm<KD, true, MB, G> : k_gemm<KD, false, MB, G>;
+  if (n224) fn = xb ? k_gemm224<KD, true, MB, G> : k_gemm224<KD, false, MB, G>;  \
+  else fn = xb ? k_gemm<KD, true, MB, G> : k_gemm<KD, false, MB, G>;
 #define QP_GEMM_AFF(KD)                                                          \
   if (mb) { if (g32) { QP_GEMM_FLAGS(KD, true, true) } else { QP_GEMM_FLAGS(KD, true, false) } } \
   else { if (g32) { QP_GEMM_FLAGS(KD, false, true) } else { QP_GEMM_FLAGS(KD, false, false) } }

@@ -48,8 +48,14 @@ bool skinny_supported(const Desc& d);
 hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M,
                          const Bufs& b, const void* bias, void* y, int ydt,
                          const size_t bytes[5], hipStream_t s);
+// Workspace bytes of the qGEMM with 224-row tiles and staged activations (M
+// rounded up to 16 rows of K fp16); 0 where 256-row tiles are as good or
+// the shape is past its 32-bit indexing.
+size_t gemm_workspace_bytes(const Desc& d, int64_t M);
+// ws: null (256-row tiles), or a device buffer of gemm_workspace_bytes(d, M)
+// > 0 bytes (a staging kernel, then the 224-row-tile kernel, same stream).
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
-                       hipStream_t s);
+                       void* ws, hipStream_t s);
 
 }  // namespace qp

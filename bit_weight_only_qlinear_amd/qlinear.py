@@ -59,6 +59,8 @@ def _load():
         "qpack_dequantize": (I32, [D, W, P, I32, P]),
         "qlinear_forward": (I32, [D, P, I32, I64, W, P, P, I32, P]),
         "qlinear_forward_kernel": (I32, [D, P, I32, I64, W, P, P, I32, I32, P]),
+        "qlinear_workspace_bytes": (I32, [D, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)]),
+        "qlinear_forward_ws": (I32, [D, P, I32, I64, W, P, P, I32, I32, P, ctypes.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -70,7 +72,8 @@ def _load():
 lib = _load()
 EXPORTED = ("qpack_abi_version", "qpack_last_error", "qpack_sizes", "qpack_quantize",
             "qpack_unpack_codes", "qpack_pack_codes", "qpack_dequantize",
-            "qlinear_forward", "qlinear_forward_kernel")
+            "qlinear_forward", "qlinear_forward_kernel", "qlinear_workspace_bytes",
+            "qlinear_forward_ws")
 
 
 @dataclass(frozen=True)
@@ -213,9 +216,22 @@ def _xdtype(t):
     raise TypeError(f"activations must be float16 or bfloat16, got {t.dtype}")
 
 
+def workspace_bytes(desc: QDesc, M: int, x_dtype: str = "bf16",
+                    kernel: int = QP_KERNEL_AUTO) -> int:
+    """Device workspace bytes qlinear_forward can use (qlinear_workspace_bytes)."""
+    d, n = desc.c(), ctypes.c_size_t(0)
+    _check(lib.qlinear_workspace_bytes(ctypes.byref(d), DTYPE_IDS[x_dtype], M, kernel,
+                                       ctypes.byref(n)))
+    return n.value
+
+
 def qlinear_forward(desc: QDesc, x, w, bias=None, y_dtype: Optional[str] = None,
-                    kernel: int = QP_KERNEL_AUTO, out=None):
-    """y [M, N] = x [M, K] W^T (+ bias).  x: fp16/bf16 device tensor."""
+                    kernel: int = QP_KERNEL_AUTO, out=None, workspace="auto"):
+    """y [M, N] = x [M, K] W^T (+ bias).  x: fp16/bf16 device tensor.
+
+    workspace: "auto" allocates what the call can use from torch's caching
+    allocator on the current stream; None runs without one; or a device
+    tensor (its bytes are the workspace)."""
     import torch
     xd = _xdtype(x)
     yd = y_dtype or xd
@@ -223,8 +239,17 @@ def qlinear_forward(desc: QDesc, x, w, bias=None, y_dtype: Optional[str] = None,
     M = x.shape[0]
     if out is None:
         out = torch.empty((M, desc.N), dtype=tdt, device=x.device)
+    buf, nbytes = None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, got {workspace!r}")
+        nbytes = workspace_bytes(desc, M, xd, kernel)
+        if nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    elif workspace is not None:
+        buf, nbytes = workspace, workspace.numel() * workspace.element_size()
     d, ws = desc.c(), _wstruct(w)
-    _check(lib.qlinear_forward_kernel(ctypes.byref(d), _ptr(x), DTYPE_IDS[xd], M,
-                                      ctypes.byref(ws), _ptr(bias), _ptr(out),
-                                      DTYPE_IDS[yd], kernel, _stream(x.device)))
+    _check(lib.qlinear_forward_ws(ctypes.byref(d), _ptr(x), DTYPE_IDS[xd], M,
+                                  ctypes.byref(ws), _ptr(bias), _ptr(out), DTYPE_IDS[yd],
+                                  kernel, _ptr(buf), nbytes, _stream(x.device)))
     return out

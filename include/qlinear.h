@@ -206,6 +206,34 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x,
                                  const qp_weights* w, const void* bias, void* y,
                                  int32_t y_dtype, int32_t kernel, void* stream);
 
+/* Host only.  Bytes of device workspace that qlinear_forward_ws can use for
+ * these arguments (the kernel is chosen as in qlinear_forward_kernel).  The
+ * qGEMM has a second tiling, 224 weight rows per block instead of 256, for
+ * shapes whose block count it spreads better over the 256 compute units
+ * (N = 14336 at M = 2048: 512 blocks, two full waves, instead of 448, 1.75
+ * waves); it reads the activations staged once as fp16 in MFMA fragment
+ * order, ceil(M / 16) * 16 * K * 2 bytes.  0 when the call would not use
+ * it (another kernel, 256-row tiles, or more than 2^31 staged bytes).  The
+ * argument checks of the forward call apply. */
+qp_status qlinear_workspace_bytes(const qp_desc* d, int32_t x_dtype, int64_t M,
+                                  int32_t kernel, size_t* bytes);
+
+/* qlinear_forward_kernel with a caller-owned device workspace (16-byte
+ * aligned).  When qlinear_workspace_bytes gives n > 0, a non-NULL workspace
+ * of at least n bytes selects the 224-row-tile qGEMM: a staging kernel
+ * writes the workspace, then the qGEMM reads it, both on `stream`; a
+ * smaller non-zero size is QP_EINVAL.  Same numerics as the 256-row-tile
+ * qGEMM (fp16 operands, fp32 accumulation) with another MFMA shape, so the
+ * two agree up to the order of fp32 additions.  The workspace is busy until
+ * this call's kernels finish on `stream`: work on other streams must not
+ * use it meanwhile.  With n == 0 or a NULL workspace the call is
+ * qlinear_forward_kernel. */
+qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype,
+                             int64_t M, const qp_weights* w, const void* bias,
+                             void* y, int32_t y_dtype, int32_t kernel,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -137,3 +137,40 @@ def test_other_entry_points_validate(q):
     assert "out_dtype" in _err(q)
     assert q.lib.qpack_sizes(None, None) == q.QP_EINVAL
     assert q.lib.qpack_sizes(ctypes.byref(d), None) == q.QP_EINVAL
+
+
+def test_workspace_query_and_checks(q):
+    n = ctypes.c_size_t(7)
+    d = q.QDesc.affine(64, 512).c()
+    # qGEMM: M rounded up to 32 rows of K fp16; other kernels take none
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 300, 2, ctypes.byref(n)) == q.QP_OK
+    assert n.value == 304 * 512 * 2
+    # 8192 rows at M = 2048: 256 blocks of 256 rows (one wave) beat 296
+    # blocks of 224 rows (two waves): no workspace
+    d8 = q.QDesc.affine(8192, 512).c()
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d8), 1, 2048, 0, ctypes.byref(n)) == q.QP_OK
+    assert n.value == 0
+    # 14336 rows at M = 2048: 512 blocks of 224 rows beat 448 of 256
+    d14 = q.QDesc.affine(14336, 4096).c()
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d14), 1, 2048, 0, ctypes.byref(n)) == q.QP_OK
+    assert n.value == 2048 * 4096 * 2
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 1, 0, ctypes.byref(n)) == q.QP_OK
+    assert n.value == 0
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 4, 1, ctypes.byref(n)) == q.QP_OK
+    assert n.value == 0
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 0, 2, ctypes.byref(n)) == q.QP_ESHAPE
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 64, 2, None) == q.QP_EINVAL
+    # past 2^31 staged bytes the qGEMM runs without a workspace
+    big = q.QDesc.affine(64, 1 << 16).c()
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(big), 1, 1 << 15, 2,
+                                         ctypes.byref(n)) == q.QP_OK
+    assert n.value == 0
+    w = q._Weights(FAKE, None, FAKE, FAKE, None)
+
+    def fwd(ws, nbytes, M=64, kernel=2):
+        return q.lib.qlinear_forward_ws(ctypes.byref(d), ctypes.c_void_p(FAKE), 1, M,
+                                        ctypes.byref(w), None, ctypes.c_void_p(FAKE), 1,
+                                        kernel, ctypes.c_void_p(ws), nbytes, None)
+    assert fwd(FAKE, 16) == q.QP_EINVAL and "workspace too small" in _err(q)
+    assert fwd(FAKE + 8, 1 << 20) == q.QP_EALIGN and "workspace" in _err(q)
+    assert fwd(FAKE, 16, M=0) == q.QP_ESHAPE

@@ -120,7 +120,8 @@ def test_quantize_exhaustive_codes_roundtrip(q):
 
 
 # --------------------------------------------------------------- forward
-def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_weights=False):
+def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_weights=False,
+                  workspace="auto"):
     W = _weights(d.N, d.K, seed)
     rng = np.random.default_rng(seed + 1)
     xb = synth.draw_activations(rng, M, d.K, xdtype)
@@ -130,7 +131,7 @@ def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_
     xd = to_dev_bits(xb, xdtype)
     bias_bits = synth.random_bias_bits(seed, d.N, xdtype) if with_bias else None
     bd = to_dev_bits(bias_bits, xdtype) if with_bias else None
-    y = q.qlinear_forward(d, xd, buf, bias=bd, y_dtype=ydt, kernel=kernel)
+    y = q.qlinear_forward(d, xd, buf, bias=bd, y_dtype=ydt, kernel=kernel, workspace=workspace)
     torch.cuda.synchronize()
     qz = oracle.quantize(W, f)
     w64 = oracle.dequant_f64(qz, f)
@@ -192,9 +193,41 @@ def test_gemm_forward(q, N, K, M):
         if K % 64:
             continue
         for xdt, ydt in [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16")]:
-            print("gemm", _id(d), M, xdt, ydt, flush=True)
-            _forward_case(q, d, M, xdt, ydt, q.QP_KERNEL_GEMM, seed=N * 17 + K + M + i,
-                          with_bias=(i % 2 == 1))
+            for ws in ("auto", None):   # 224-row tiles where they pay, 256-row tiles
+                print("gemm", _id(d), M, xdt, ydt, ws, flush=True)
+                _forward_case(q, d, M, xdt, ydt, q.QP_KERNEL_GEMM, seed=N * 17 + K + M + i,
+                              with_bias=(i % 2 == 1), workspace=ws)
+
+
+@pytest.mark.parametrize("N,K,M", [(130, 512, 1), (257, 1280, 33), (520, 768, 300),
+                                   (64, 4096, 257)])
+def test_gemm_workspace_tilings_agree(q, N, K, M):
+    """224-row tiles (staged activations) and 256-row tiles: same fp16
+    operands, fp32 sums in another order; a workspace full of NaN bytes
+    checks that the staging writes every byte the kernel reads."""
+    for i, d in enumerate(_descs(q, N, K)):
+        for xdt in ("bf16", "f16"):
+            print("gemm workspace", _id(d), M, xdt, flush=True)
+            W = _weights(N, K, 5 + i)
+            xb = synth.draw_activations(np.random.default_rng(M + i), M, K, xdt)
+            buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
+            xd = to_dev_bits(xb, xdt)
+            nb = q.workspace_bytes(d, M, xdt, q.QP_KERNEL_GEMM)
+            assert nb == (M + 15) // 16 * 16 * K * 2
+            ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+            y0 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM,
+                                   workspace=None)
+            y1 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM,
+                                   workspace=ws)
+            y2 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM)
+            torch.cuda.synchronize()
+            assert torch.isfinite(y1).all()
+            assert torch.equal(y1, y2)
+            # |difference| <= K * 2^-23 * sum |w x| bounds two fp32 summation orders
+            wd = q.qpack_dequantize(d, buf, "f16").float()
+            xf = xd.float()
+            bound = K * 2.0 ** -23 * (xf.abs() @ wd.abs().T) + 1e-30
+            assert ((y0 - y1).abs() <= bound).all()
 
 
 def test_auto_dispatch_matches(q):
