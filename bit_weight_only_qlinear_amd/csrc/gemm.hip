@@ -143,7 +143,7 @@ struct Rsrc {
 // Every offset is a per-lane (voffset) offset, so the buffer range check
 // covers all of it: steps at or past K (the pipeline's two phantom steps)
 // read either the next row's data or 0, never memory outside the buffers.
-template <int KIND, bool GS32, bool LOADX = true>
+template <int KIND, bool GS32, bool LOADX = true, bool LOADMETA = true>
 __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int kt,
                                            Stage<KIND>& st) {
   if constexpr (LOADX) {
@@ -167,6 +167,7 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int
     }
   }
   st.s0 = st.s1 = st.s2 = 0;
+  if constexpr (!LOADMETA) return;
   const uint32_t g2 = 2u * (uint32_t)kt + r.half;   // this half's group of 32
   if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
     const uint32_t g = GS32 ? g2 : (uint32_t)kt * BK / (uint32_t)a.gs;
@@ -588,7 +589,12 @@ __global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
   xf[c] = act_chunk<XBF16>(u);
 }
 
-template <int KIND, bool XBF16, bool MBF16, bool GS32>
+// MCH (affine, group size 64, K % 512 == 0): the scales and biases come in
+// 16-byte chunks of 8 groups, one chunk per 8 steps, loaded a chunk ahead
+// into a two-slot register ring (per step, two 2-byte loads that touch 32
+// cache lines per wave cost more than the MFMAs can hide); the step loop is
+// unrolled by 16 so that slot and element are compile-time constants.
+template <int KIND, bool XBF16, bool MBF16, bool GS32, bool MCH>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm224(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
@@ -656,9 +662,34 @@ k_gemm224(GemmArgs a) {
   // `fre` and B fragment loads of step kt + 1.  Phantom steps at the end
   // stay inside the buffers (range-checked offsets), as in k_gemm.
   // Instruction order is pinned with scheduling fences.
-  auto kstep = [&](int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
+  // metadata chunks (MCH): [slot][scales, biases]; chunk c = groups 8c ..
+  // 8c + 7 of the thread's row, in slot c & 1
+  uint4 mc[2][2];
+  auto ld_chunk = [&](int c, uint4 (&dst)[2]) {
+    dst[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r.s, r.so + 16u * (uint32_t)c, 0, 0));
+    dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           r.z, r.zo + 16u * (uint32_t)c, 0, 0));
+  };
+  // raw scale and bias of step t (t % 16 == tu) into a stage
+  auto set_meta = [&](auto TU, Stage<KIND>& st) {
+    constexpr int tu = decltype(TU)::value;
+    constexpr int slot = (tu >> 3) & 1, e = tu & 7;
+    st.s0 = (mc[slot][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    st.s1 = (mc[slot][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  };
+
+  // U: position of step kt in the unrolled loop (kt % 16 == U for MCH)
+  auto kstep = [&](auto U, int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
+    constexpr int u = decltype(U)::value;
     const uint32_t cur = (uint32_t)(kt & 1);
-    load_stage<KIND, GS32, false>(a, r, kt + 2, fre);
+    load_stage<KIND, GS32, false, !MCH>(a, r, kt + 2, fre);
+    if constexpr (MCH) {
+      // at steps 8c' (chunk c' starts) load chunk c' + 1 into the slot that
+      // chunk c' - 1 held: its last step (8c' - 1) was converted already
+      if constexpr (u % 8 == 0) ld_chunk(kt / 8 + 1, mc[((u >> 3) + 1) & 1]);
+      set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
+    }
     __builtin_amdgcn_sched_barrier(0);
     half8_t A[7];
 #pragma unroll
@@ -694,8 +725,13 @@ k_gemm224(GemmArgs a) {
   };
 
   Stage<KIND> st0, st1;
-  load_stage<KIND, GS32, false>(a, r, 0, st0);
-  load_stage<KIND, GS32, false>(a, r, 1, st1);
+  load_stage<KIND, GS32, false, !MCH>(a, r, 0, st0);
+  load_stage<KIND, GS32, false, !MCH>(a, r, 1, st1);
+  if constexpr (MCH) {
+    ld_chunk(0, mc[0]);
+    ld_chunk(1, mc[1]);
+    set_meta(std::integral_constant<int, 0>{}, st0);
+  }
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -703,9 +739,21 @@ k_gemm224(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) st_w(0u, p, weight_chunk<KIND, MBF16>(st0, p, magic));
   __syncthreads();
-  for (int kt = 0; kt < KT; kt += 2) {
-    kstep(kt, st0, st1);
-    if (kt + 1 < KT) kstep(kt + 1, st1, st0);
+  if constexpr (MCH) {
+    for (int kt = 0; kt < KT; kt += 16) {
+      static_for<16>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        if (u == 0 || kt + u < KT) {
+          if constexpr (u % 2 == 0) kstep(U, kt + u, st0, st1);
+          else kstep(U, kt + u, st1, st0);
+        }
+      });
+    }
+  } else {
+    for (int kt = 0; kt < KT; kt += 2) {
+      kstep(std::integral_constant<int, 0>{}, kt, st0, st1);
+      if (kt + 1 < KT) kstep(std::integral_constant<int, 1>{}, kt + 1, st1, st0);
+    }
   }
 
   // ---- epilogue: lane holds rows n = 16 i + 4 (lane >> 4) + v (v = 0..3)
@@ -1261,14 +1309,18 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
+  const bool mch = d.fmt == AFFINE && d.gs == 64 && d.K % 512 == 0;
   void (*fn)(GemmArgs) = nullptr;
   // (kind, x dtype, metadata dtype, two groups per 64-column step)
 #define QP_GEMM_FLAGS(KD, MB, G)                                                 \
-  if (n224) fn = xb ? k_gemm224<KD, true, MB, G> : k_gemm224<KD, false, MB, G>;  \
+  if (n224) fn = xb ? k_gemm224<KD, true, MB, G, false> : k_gemm224<KD, false, MB, G, false>;  \
   else fn = xb ? k_gemm<KD, true, MB, G> : k_gemm<KD, false, MB, G>;
+#define QP_GEMM_FLAGS_CH(KD, MB)                                                 \
+  if (n224 && mch) fn = xb ? k_gemm224<KD, true, MB, false, true> : k_gemm224<KD, false, MB, false, true>; \
+  else { QP_GEMM_FLAGS(KD, MB, false) }
 #define QP_GEMM_AFF(KD)                                                          \
-  if (mb) { if (g32) { QP_GEMM_FLAGS(KD, true, true) } else { QP_GEMM_FLAGS(KD, true, false) } } \
-  else { if (g32) { QP_GEMM_FLAGS(KD, false, true) } else { QP_GEMM_FLAGS(KD, false, false) } }
+  if (mb) { if (g32) { QP_GEMM_FLAGS(KD, true, true) } else { QP_GEMM_FLAGS_CH(KD, true) } } \
+  else { if (g32) { QP_GEMM_FLAGS(KD, false, true) } else { QP_GEMM_FLAGS_CH(KD, false) } }
   if (d.fmt == AFFINE) {
     if (d.bits == 2) { QP_GEMM_AFF(G_AFF2) }
     else if (d.bits == 4) { QP_GEMM_AFF(G_AFF4) }
@@ -1281,6 +1333,7 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
     if (g32) { QP_GEMM_FLAGS(G_SYM4, false, true) } else { QP_GEMM_FLAGS(G_SYM4, false, false) }
   }
 #undef QP_GEMM_AFF
+#undef QP_GEMM_FLAGS_CH
 #undef QP_GEMM_FLAGS
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();

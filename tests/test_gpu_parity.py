@@ -186,7 +186,8 @@ def test_gemv_mfma_large_k(q, fmt):
                       f16_weights=True)
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768)])
+@pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768),
+                                 (72, 1536)])
 @pytest.mark.parametrize("M", [1, 9, 64, 130, 300])
 def test_gemm_forward(q, N, K, M):
     for i, d in enumerate(_descs(q, N, K)):
