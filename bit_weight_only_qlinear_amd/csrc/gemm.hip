@@ -702,8 +702,8 @@ k_gemm224(GemmArgs a) {
         for (int i = 0; i < 7; ++i) An[i] = rd_a(cur, 1, i);
       }
       __builtin_amdgcn_sched_barrier(0);
-      const uint4 w0 = weight_chunk<KIND, MBF16>(nxt, 2 * sub, magic);
-      const uint4 w1 = weight_chunk<KIND, MBF16>(nxt, 2 * sub + 1, magic);
+      uint4 w0 = weight_chunk<KIND, MBF16>(nxt, 2 * sub, magic);
+      uint4 w1 = weight_chunk<KIND, MBF16>(nxt, 2 * sub + 1, magic);
       static_for<7>([&](auto I) {
         constexpr int i = decltype(I)::value;
         static_for<4>([&](auto J) {
@@ -711,6 +711,11 @@ k_gemm224(GemmArgs a) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], Bf[sub][j], acc[i][j], 0, 0, 0);
         });
       });
+      // the dequantized chunks are complete here, so their VALU work stays
+      // among the MFMAs (LLVM would otherwise sink it next to the LDS store,
+      // after the last MFMA)
+      asm volatile("" : "+v"(w0.x), "+v"(w0.y), "+v"(w0.z), "+v"(w0.w), "+v"(w1.x), "+v"(w1.y),
+                   "+v"(w1.z), "+v"(w1.w));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(kt + 1, sub, j);
