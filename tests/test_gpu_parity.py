@@ -231,6 +231,38 @@ def test_gemm_workspace_tilings_agree(q, N, K, M):
             assert ((y0 - y1).abs() <= bound).all()
 
 
+@pytest.mark.parametrize("M,kernel,ws", [(1, 0, "auto"), (8, 3, "auto"), (300, 2, "auto"),
+                                          (300, 2, None)])
+def test_graph_replay_matches_eager(q, M, kernel, ws):
+    """A captured forward (the qGEMM's workspace is allocated inside the
+    capture, from the graph's pool) replayed several times, with eager work
+    and synchronizations in between, gives the eager result bit for bit."""
+    d = q.QDesc.affine(520, 1024, 4, 64, "bf16")
+    W = _weights(d.N, d.K, 11)
+    buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
+    xd = to_dev_bits(synth.draw_activations(np.random.default_rng(M), M, d.K, "bf16"), "bf16")
+    ref = q.qlinear_forward(d, xd, buf, kernel=kernel, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        q.qlinear_forward(d, xd, buf, kernel=kernel, out=y, workspace=ws)   # warm-up
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlinear_forward(d, xd, buf, kernel=kernel, out=y, workspace=ws)
+    other = torch.zeros(1 << 20, device="cuda")
+    for rep in range(4):
+        y.fill_(float("nan"))
+        other.add_(1.0)                      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), rep
+
+
 def test_auto_dispatch_matches(q):
     d = q.QDesc.affine(200, 1024)
     for M in (1, 8, 9, 33):
