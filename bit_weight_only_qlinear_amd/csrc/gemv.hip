@@ -178,7 +178,7 @@ __device__ __forceinline__ uint32_t pair_bytes13(uint32_t codes, uint32_t magic)
 #define QP_GEMV_MIN_WAVES_PER_EU 2
 #endif
 #ifndef QP_GEMV_EARLY_ROWS
-#define QP_GEMV_EARLY_ROWS 2        // first-batch rows requested before the prologue wait
+#define QP_GEMV_EARLY_ROWS 3        // first-batch rows requested before the prologue wait
 #endif
 
 __host__ __device__ constexpr int single_loads(int k) {
