@@ -679,6 +679,24 @@ k_gemm224(GemmArgs a) {
     st.s1 = (mc[slot][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
   };
 
+  // The last ND A groups of a step's second substep run after the barrier,
+  // at the top of the next step, where both waves of a SIMD would otherwise
+  // wait for their first LDS fragments (register operands only: the
+  // fragments are kept in Ad, the substep's B fragments stay in Bf[1] and
+  // are reloaded after them).  int8 keeps ND = 0 (register budget).
+  constexpr int ND = KIND == G_AFF8 ? 0 : 3;
+  half8_t Ad[ND > 0 ? ND : 1];
+  auto mfma_deferred = [&]() {
+    static_for<ND>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        acc[7 - ND + i][j] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(Ad[i], Bf[1][j], acc[7 - ND + i][j], 0, 0, 0);
+      });
+    });
+  };
+
   // U: position of step kt in the unrolled loop (kt % 16 == U for MCH)
   auto kstep = [&](auto U, int kt, Stage<KIND>& fre, Stage<KIND>& nxt) {
     constexpr int u = decltype(U)::value;
@@ -694,6 +712,12 @@ k_gemm224(GemmArgs a) {
     half8_t A[7];
 #pragma unroll
     for (int i = 0; i < 7; ++i) A[i] = rd_a(cur, 0, i);
+    if constexpr (ND > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt > 0) mfma_deferred();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Bf[1][j] = ld_b(kt, 1, j);
+    }
     static_for<2>([&](auto SUB) {
       constexpr int sub = decltype(SUB)::value;
       half8_t An[7];
@@ -704,21 +728,27 @@ k_gemm224(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       uint4 w0 = weight_chunk<KIND, MBF16>(nxt, 2 * sub, magic);
       uint4 w1 = weight_chunk<KIND, MBF16>(nxt, 2 * sub + 1, magic);
-      static_for<7>([&](auto I) {
+      static_for<(sub == 1 ? 7 - ND : 7)>([&](auto I) {
         constexpr int i = decltype(I)::value;
         static_for<4>([&](auto J) {
           constexpr int j = decltype(J)::value;
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], Bf[sub][j], acc[i][j], 0, 0, 0);
         });
       });
+      if constexpr (sub == 1 && ND > 0) {
+#pragma unroll
+        for (int i = 0; i < ND; ++i) Ad[i] = A[7 - ND + i];
+      }
       // the dequantized chunks are complete here, so their VALU work stays
       // among the MFMAs (LLVM would otherwise sink it next to the LDS store,
       // after the last MFMA)
       asm volatile("" : "+v"(w0.x), "+v"(w0.y), "+v"(w0.z), "+v"(w0.w), "+v"(w1.x), "+v"(w1.y),
                    "+v"(w1.z), "+v"(w1.w));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (sub == 0 || ND == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(kt + 1, sub, j);
+        for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(kt + 1, sub, j);
+      }
       st_w(cur ^ 1u, 2 * sub, w0);
       st_w(cur ^ 1u, 2 * sub + 1, w1);
       if constexpr (sub == 0) {
@@ -760,6 +790,7 @@ k_gemm224(GemmArgs a) {
       if (kt + 1 < KT) kstep(std::integral_constant<int, 1>{}, kt + 1, st1, st0);
     }
   }
+  if constexpr (ND > 0) mfma_deferred();   // the last step's deferred groups
 
   // ---- epilogue: lane holds rows n = 16 i + 4 (lane >> 4) + v (v = 0..3)
   // of column m = 16 j + (lane & 15) of the wave's tiles.
