@@ -589,12 +589,14 @@ __global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
   xf[c] = act_chunk<XBF16>(u);
 }
 
-// MCH (affine, group size 64, K % 512 == 0): the scales and biases come in
-// 16-byte chunks of 8 groups, one chunk per 8 steps, loaded a chunk ahead
-// into a two-slot register ring (per step, two 2-byte loads that touch 32
-// cache lines per wave cost more than the MFMAs can hide); the step loop is
-// unrolled by 16 so that slot and element are compile-time constants.
-template <int KIND, bool XBF16, bool MBF16, bool GS32, bool MCH>
+// MCH = group size (affine, 64 with K % 512 == 0 or 32 with K % 256 == 0;
+// else 0): the scales and biases come in 16-byte chunks of 8 groups (one
+// chunk per 8 or 4 steps) loaded a chunk ahead into a two-slot register ring
+// (per step, two 2-byte loads that touch 32 cache lines per wave cost more
+// than the MFMAs can hide); the step loop is unrolled by 16 so that slot
+// and element are compile-time constants (group size 32: the element also
+// depends on the thread's half row).
+template <int KIND, bool XBF16, bool MBF16, bool GS32, int MCH>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm224(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
@@ -671,12 +673,22 @@ k_gemm224(GemmArgs a) {
     dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            r.z, r.zo + 16u * (uint32_t)c, 0, 0));
   };
-  // raw scale and bias of step t (t % 16 == tu) into a stage
+  // raw scale and bias of step t (t % 16 == tu) into a stage: group t
+  // (group size 64) or 2t + half (group size 32) of the thread's row
+  constexpr int MP = MCH == 32 ? 4 : 8;   // steps per chunk
+  const uint32_t msh = 16u * (uint32_t)(tid & 1);
   auto set_meta = [&](auto TU, Stage<KIND>& st) {
     constexpr int tu = decltype(TU)::value;
-    constexpr int slot = (tu >> 3) & 1, e = tu & 7;
-    st.s0 = (mc[slot][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-    st.s1 = (mc[slot][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    constexpr int slot = (tu / MP) & 1;
+    if constexpr (MCH == 32) {
+      constexpr int w = tu & 3;
+      st.s0 = (mc[slot][0][w] >> msh) & 0xFFFFu;
+      st.s1 = (mc[slot][1][w] >> msh) & 0xFFFFu;
+    } else {
+      constexpr int e = tu & 7;
+      st.s0 = (mc[slot][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      st.s1 = (mc[slot][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    }
   };
 
   // The last ND A groups of a step's second substep run after the barrier,
@@ -703,9 +715,9 @@ k_gemm224(GemmArgs a) {
     const uint32_t cur = (uint32_t)(kt & 1);
     load_stage<KIND, GS32, false, !MCH>(a, r, kt + 2, fre);
     if constexpr (MCH) {
-      // at steps 8c' (chunk c' starts) load chunk c' + 1 into the slot that
-      // chunk c' - 1 held: its last step (8c' - 1) was converted already
-      if constexpr (u % 8 == 0) ld_chunk(kt / 8 + 1, mc[((u >> 3) + 1) & 1]);
+      // where chunk c' starts (step MP c') load chunk c' + 1 into the slot
+      // that chunk c' - 1 held: its last step was converted already
+      if constexpr (u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
       set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1345,18 +1357,20 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
-  const bool mch = d.fmt == AFFINE && d.gs == 64 && d.K % 512 == 0;
+  // chunked affine metadata: whole 8-group chunks per row (16-byte aligned)
+  const bool mch = d.fmt == AFFINE && ((d.gs == 64 && d.K % 512 == 0) ||
+                                       (d.gs == 32 && d.K % 256 == 0));
   void (*fn)(GemmArgs) = nullptr;
   // (kind, x dtype, metadata dtype, two groups per 64-column step)
 #define QP_GEMM_FLAGS(KD, MB, G)                                                 \
-  if (n224) fn = xb ? k_gemm224<KD, true, MB, G, false> : k_gemm224<KD, false, MB, G, false>;  \
+  if (n224) fn = xb ? k_gemm224<KD, true, MB, G, 0> : k_gemm224<KD, false, MB, G, 0>;  \
   else fn = xb ? k_gemm<KD, true, MB, G> : k_gemm<KD, false, MB, G>;
-#define QP_GEMM_FLAGS_CH(KD, MB)                                                 \
-  if (n224 && mch) fn = xb ? k_gemm224<KD, true, MB, false, true> : k_gemm224<KD, false, MB, false, true>; \
-  else { QP_GEMM_FLAGS(KD, MB, false) }
+#define QP_GEMM_FLAGS_CH(KD, MB, G, GSZ)                                         \
+  if (n224 && mch) fn = xb ? k_gemm224<KD, true, MB, G, GSZ> : k_gemm224<KD, false, MB, G, GSZ>; \
+  else { QP_GEMM_FLAGS(KD, MB, G) }
 #define QP_GEMM_AFF(KD)                                                          \
-  if (mb) { if (g32) { QP_GEMM_FLAGS(KD, true, true) } else { QP_GEMM_FLAGS_CH(KD, true) } } \
-  else { if (g32) { QP_GEMM_FLAGS(KD, false, true) } else { QP_GEMM_FLAGS_CH(KD, false) } }
+  if (mb) { if (g32) { QP_GEMM_FLAGS_CH(KD, true, true, 32) } else { QP_GEMM_FLAGS_CH(KD, true, false, 64) } } \
+  else { if (g32) { QP_GEMM_FLAGS_CH(KD, false, true, 32) } else { QP_GEMM_FLAGS_CH(KD, false, false, 64) } }
   if (d.fmt == AFFINE) {
     if (d.bits == 2) { QP_GEMM_AFF(G_AFF2) }
     else if (d.bits == 4) { QP_GEMM_AFF(G_AFF4) }
