@@ -673,14 +673,25 @@ k_gemm224(GemmArgs a) {
     dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            r.z, r.zo + 16u * (uint32_t)c, 0, 0));
   };
-  // raw scale and bias of step t (t % 16 == tu) into a stage: group t
-  // (group size 64) or 2t + half (group size 32) of the thread's row
-  constexpr int MP = MCH == 32 ? 4 : 8;   // steps per chunk
-  const uint32_t msh = 16u * (uint32_t)(tid & 1);
+  // Q4K: chunks of 16 uint8 scale and zero codes (8 steps), and the
+  // super-block step word once per 4 steps into a two-slot ring
+  uint32_t ms[2];
+  auto ld_step = [&](int b, uint32_t& dst) {
+    dst = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + 4u * (uint32_t)b, 0, 0);
+  };
+  // raw metadata of step t (t % 16 == tu) into a stage: group t (group size
+  // 64) or 2t + half (group size 32, Q4K) of the thread's row
+  constexpr int MP = (MCH == 32 && KIND != G_Q4K) ? 4 : 8;   // steps per chunk
+  const uint32_t msh = (KIND == G_Q4K ? 8u : 16u) * (uint32_t)(tid & 1);
   auto set_meta = [&](auto TU, Stage<KIND>& st) {
     constexpr int tu = decltype(TU)::value;
     constexpr int slot = (tu / MP) & 1;
-    if constexpr (MCH == 32) {
+    if constexpr (KIND == G_Q4K) {
+      constexpr int w = (tu & 7) >> 1, sh = 16 * (tu & 1);
+      st.s0 = (mc[slot][0][w] >> (msh + sh)) & 0xFFu;
+      st.s1 = (mc[slot][1][w] >> (msh + sh)) & 0xFFu;
+      st.s2 = ms[(tu >> 2) & 1];
+    } else if constexpr (MCH == 32) {
       constexpr int w = tu & 3;
       st.s0 = (mc[slot][0][w] >> msh) & 0xFFFFu;
       st.s1 = (mc[slot][1][w] >> msh) & 0xFFFFu;
@@ -695,8 +706,9 @@ k_gemm224(GemmArgs a) {
   // at the top of the next step, where both waves of a SIMD would otherwise
   // wait for their first LDS fragments (register operands only: the
   // fragments are kept in Ad, the substep's B fragments stay in Bf[1] and
-  // are reloaded after them).  int8 keeps ND = 0 (register budget).
-  constexpr int ND = KIND == G_AFF8 ? 0 : 3;
+  // are reloaded after them).  int8 and chunked Q4K keep ND = 0 (register
+  // budget).
+  constexpr int ND = (KIND == G_AFF8 || (KIND == G_Q4K && MCH)) ? 0 : 3;
   half8_t Ad[ND > 0 ? ND : 1];
   auto mfma_deferred = [&]() {
     static_for<ND>([&](auto I) {
@@ -718,6 +730,8 @@ k_gemm224(GemmArgs a) {
       // where chunk c' starts (step MP c') load chunk c' + 1 into the slot
       // that chunk c' - 1 held: its last step was converted already
       if constexpr (u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
+      // Q4K step words: super-block b' + 1 at step 4b' (same argument)
+      if constexpr (KIND == G_Q4K && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
       set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -777,6 +791,10 @@ k_gemm224(GemmArgs a) {
   if constexpr (MCH) {
     ld_chunk(0, mc[0]);
     ld_chunk(1, mc[1]);
+    if constexpr (KIND == G_Q4K) {
+      ld_step(0, ms[0]);
+      ld_step(1, ms[1]);
+    }
     set_meta(std::integral_constant<int, 0>{}, st0);
   }
 #pragma unroll
@@ -1376,7 +1394,9 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
     else if (d.bits == 4) { QP_GEMM_AFF(G_AFF4) }
     else { QP_GEMM_AFF(G_AFF8) }
   } else if (d.fmt == Q4K) {
-    QP_GEMM_FLAGS(G_Q4K, false, false)
+    if (n224 && d.K % 512 == 0)
+      fn = xb ? k_gemm224<G_Q4K, true, false, false, 32> : k_gemm224<G_Q4K, false, false, false, 32>;
+    else { QP_GEMM_FLAGS(G_Q4K, false, false) }
   } else if (d.fmt == Q6K) {
     QP_GEMM_FLAGS(G_Q6K, false, false)
   } else {
