@@ -167,6 +167,11 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int
     }
   }
   st.s0 = st.s1 = st.s2 = 0;
+  if constexpr (KIND == G_Q6K) {   // high code plane (codes, not metadata)
+    const uint2 v = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho + (uint32_t)kt * 16u, 0, 0));
+    st.h[0] = v.x; st.h[1] = v.y;
+  }
   if constexpr (!LOADMETA) return;
   const uint32_t g2 = 2u * (uint32_t)kt + r.half;   // this half's group of 32
   if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
@@ -179,9 +184,6 @@ __device__ __forceinline__ void load_stage(const GemmArgs& a, const Rsrc& r, int
     st.s1 = __builtin_amdgcn_raw_buffer_load_b8(r.z, r.zo + g2, 0, 0);
     st.s2 = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + (uint32_t)(kt / 4) * 4u, 0, 0);
   } else if constexpr (KIND == G_Q6K) {
-    const uint2 v = __builtin_bit_cast(
-        uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho + (uint32_t)kt * 16u, 0, 0));
-    st.h[0] = v.x; st.h[1] = v.y;
     // two int8 scale codes (groups of 16), the super-block fp16 step
     st.s0 = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so + 2u * g2, 0, 0);
     st.s2 = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po + (uint32_t)(kt / 4) * 2u, 0, 0);
@@ -670,23 +672,36 @@ k_gemm224(GemmArgs a) {
   auto ld_chunk = [&](int c, uint4 (&dst)[2]) {
     dst[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            r.s, r.so + 16u * (uint32_t)c, 0, 0));
-    dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           r.z, r.zo + 16u * (uint32_t)c, 0, 0));
+    if constexpr (KIND != G_Q6K)   // Q6K has no second array
+      dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             r.z, r.zo + 16u * (uint32_t)c, 0, 0));
   };
   // Q4K: chunks of 16 uint8 scale and zero codes (8 steps), and the
-  // super-block step word once per 4 steps into a two-slot ring
+  // super-block step word once per 4 steps into a two-slot ring.  Q6K:
+  // chunks of 16 int8 scale codes (4 steps; two per half row and step), the
+  // fp16 step once per 4 steps.  Per-channel SYM4 (MCH == 1): the row's one
+  // scale, loaded once.
   uint32_t ms[2];
   auto ld_step = [&](int b, uint32_t& dst) {
-    dst = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + 4u * (uint32_t)b, 0, 0);
+    if constexpr (KIND == G_Q6K)
+      dst = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po + 2u * (uint32_t)b, 0, 0);
+    else
+      dst = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po + 4u * (uint32_t)b, 0, 0);
   };
+  constexpr bool STEPW = KIND == G_Q4K || KIND == G_Q6K;   // step words in ms
   // raw metadata of step t (t % 16 == tu) into a stage: group t (group size
   // 64) or 2t + half (group size 32, Q4K) of the thread's row
-  constexpr int MP = (MCH == 32 && KIND != G_Q4K) ? 4 : 8;   // steps per chunk
+  constexpr int MP = ((MCH == 32 && KIND != G_Q4K) || KIND == G_Q6K) ? 4 : 8;   // steps per chunk
   const uint32_t msh = (KIND == G_Q4K ? 8u : 16u) * (uint32_t)(tid & 1);
   auto set_meta = [&](auto TU, Stage<KIND>& st) {
     constexpr int tu = decltype(TU)::value;
     constexpr int slot = (tu / MP) & 1;
-    if constexpr (KIND == G_Q4K) {
+    if constexpr (KIND == G_SYM4) {
+      st.s0 = ms[0];
+    } else if constexpr (KIND == G_Q6K) {
+      st.s0 = (mc[slot][0][tu & 3] >> msh) & 0xFFFFu;
+      st.s2 = ms[(tu >> 2) & 1];
+    } else if constexpr (KIND == G_Q4K) {
       constexpr int w = (tu & 7) >> 1, sh = 16 * (tu & 1);
       st.s0 = (mc[slot][0][w] >> (msh + sh)) & 0xFFu;
       st.s1 = (mc[slot][1][w] >> (msh + sh)) & 0xFFu;
@@ -706,9 +721,9 @@ k_gemm224(GemmArgs a) {
   // at the top of the next step, where both waves of a SIMD would otherwise
   // wait for their first LDS fragments (register operands only: the
   // fragments are kept in Ad, the substep's B fragments stay in Bf[1] and
-  // are reloaded after them).  int8 and chunked Q4K keep ND = 0 (register
+  // are reloaded after them).  int8 and chunked Q4K / Q6K keep ND = 0 (register
   // budget).
-  constexpr int ND = (KIND == G_AFF8 || (KIND == G_Q4K && MCH)) ? 0 : 3;
+  constexpr int ND = (KIND == G_AFF8 || ((KIND == G_Q4K || KIND == G_Q6K) && MCH)) ? 0 : 3;
   half8_t Ad[ND > 0 ? ND : 1];
   auto mfma_deferred = [&]() {
     static_for<ND>([&](auto I) {
@@ -729,9 +744,9 @@ k_gemm224(GemmArgs a) {
     if constexpr (MCH) {
       // where chunk c' starts (step MP c') load chunk c' + 1 into the slot
       // that chunk c' - 1 held: its last step was converted already
-      if constexpr (u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
-      // Q4K step words: super-block b' + 1 at step 4b' (same argument)
-      if constexpr (KIND == G_Q4K && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
+      if constexpr (KIND != G_SYM4 && u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
+      // step words: super-block b' + 1 at step 4b' (same argument)
+      if constexpr (STEPW && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
       set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -789,9 +804,13 @@ k_gemm224(GemmArgs a) {
   load_stage<KIND, GS32, false, !MCH>(a, r, 0, st0);
   load_stage<KIND, GS32, false, !MCH>(a, r, 1, st1);
   if constexpr (MCH) {
-    ld_chunk(0, mc[0]);
-    ld_chunk(1, mc[1]);
-    if constexpr (KIND == G_Q4K) {
+    if constexpr (KIND == G_SYM4) {
+      ms[0] = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so, 0, 0);
+    } else {
+      ld_chunk(0, mc[0]);
+      ld_chunk(1, mc[1]);
+    }
+    if constexpr (STEPW) {
       ld_step(0, ms[0]);
       ld_step(1, ms[1]);
     }
@@ -1398,9 +1417,13 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
       fn = xb ? k_gemm224<G_Q4K, true, false, false, 32> : k_gemm224<G_Q4K, false, false, false, 32>;
     else { QP_GEMM_FLAGS(G_Q4K, false, false) }
   } else if (d.fmt == Q6K) {
-    QP_GEMM_FLAGS(G_Q6K, false, false)
+    if (n224)   // K % 256 == 0 always holds for Q6K
+      fn = xb ? k_gemm224<G_Q6K, true, false, false, 16> : k_gemm224<G_Q6K, false, false, false, 16>;
+    else { QP_GEMM_FLAGS(G_Q6K, false, false) }
   } else {
-    if (g32) { QP_GEMM_FLAGS(G_SYM4, false, true) } else { QP_GEMM_FLAGS(G_SYM4, false, false) }
+    if (n224 && d.gs == d.K)   // per-channel scale
+      fn = xb ? k_gemm224<G_SYM4, true, false, false, 1> : k_gemm224<G_SYM4, false, false, false, 1>;
+    else if (g32) { QP_GEMM_FLAGS(G_SYM4, false, true) } else { QP_GEMM_FLAGS(G_SYM4, false, false) }
   }
 #undef QP_GEMM_AFF
 #undef QP_GEMM_FLAGS_CH
