@@ -591,9 +591,10 @@ __global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
   xf[c] = act_chunk<XBF16>(u);
 }
 
-// MCH = group size (affine, 64 with K % 512 == 0 or 32 with K % 256 == 0;
-// else 0): the scales and biases come in 16-byte chunks of 8 groups (one
-// chunk per 8 or 4 steps) loaded a chunk ahead into a two-slot register ring
+// MCH = group size (affine, 128 with K % 1024 == 0, 64 with K % 512 == 0 or
+// 32 with K % 256 == 0; else 0): the scales and biases come in 16-byte
+// chunks of 8 groups (one chunk per 16, 8 or 4 steps) loaded a chunk ahead
+// into a two-slot register ring (group size 128: current and next chunk)
 // (per step, two 2-byte loads that touch 32 cache lines per wave cost more
 // than the MFMAs can hide); the step loop is unrolled by 16 so that slot
 // and element are compile-time constants (group size 32: the element also
@@ -693,10 +694,19 @@ k_gemm224(GemmArgs a) {
   // 64) or 2t + half (group size 32, Q4K) of the thread's row
   constexpr int MP = ((MCH == 32 && KIND != G_Q4K) || KIND == G_Q6K) ? 4 : 8;   // steps per chunk
   const uint32_t msh = (KIND == G_Q4K ? 8u : 16u) * (uint32_t)(tid & 1);
-  auto set_meta = [&](auto TU, Stage<KIND>& st) {
+  // group size 128: one chunk per 16 steps, i.e. per unrolled iteration;
+  // mc[0] holds the current chunk, mc[1] the next (NEXT: step 16 it + 16,
+  // converted in the iteration's last step)
+  auto set_meta = [&](auto TU, Stage<KIND>& st, bool next = false) {
     constexpr int tu = decltype(TU)::value;
     constexpr int slot = (tu / MP) & 1;
-    if constexpr (KIND == G_SYM4) {
+    if constexpr (MCH == 128) {
+      constexpr int e = tu >> 1;   // group of step tu within the chunk
+      const uint4& c0 = next ? mc[1][0] : mc[0][0];
+      const uint4& c1 = next ? mc[1][1] : mc[0][1];
+      st.s0 = (c0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      st.s1 = (c1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    } else if constexpr (KIND == G_SYM4) {
       st.s0 = ms[0];
     } else if constexpr (KIND == G_Q6K) {
       st.s0 = (mc[slot][0][tu & 3] >> msh) & 0xFFFFu;
@@ -744,10 +754,15 @@ k_gemm224(GemmArgs a) {
     if constexpr (MCH) {
       // where chunk c' starts (step MP c') load chunk c' + 1 into the slot
       // that chunk c' - 1 held: its last step was converted already
-      if constexpr (KIND != G_SYM4 && u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
-      // step words: super-block b' + 1 at step 4b' (same argument)
-      if constexpr (STEPW && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
-      set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
+      if constexpr (MCH == 128) {
+        if constexpr (u == 0) ld_chunk(kt / 16 + 1, mc[1]);
+        set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt, u == 15);
+      } else {
+        if constexpr (KIND != G_SYM4 && u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
+        // step words: super-block b' + 1 at step 4b' (same argument)
+        if constexpr (STEPW && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
+        set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     half8_t A[7];
@@ -806,6 +821,8 @@ k_gemm224(GemmArgs a) {
   if constexpr (MCH) {
     if constexpr (KIND == G_SYM4) {
       ms[0] = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so, 0, 0);
+    } else if constexpr (MCH == 128) {
+      ld_chunk(0, mc[0]);   // mc[1] is loaded by the first step
     } else {
       ld_chunk(0, mc[0]);
       ld_chunk(1, mc[1]);
@@ -832,6 +849,10 @@ k_gemm224(GemmArgs a) {
           else kstep(U, kt + u, st1, st0);
         }
       });
+      if constexpr (MCH == 128) {   // the next chunk becomes the current one
+        mc[0][0] = mc[1][0];
+        mc[0][1] = mc[1][1];
+      }
     }
   } else {
     for (int kt = 0; kt < KT; kt += 2) {
@@ -1395,8 +1416,10 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
   // chunked affine metadata: whole 8-group chunks per row (16-byte aligned)
+  const bool g128 = d.gs == 128;
   const bool mch = d.fmt == AFFINE && ((d.gs == 64 && d.K % 512 == 0) ||
-                                       (d.gs == 32 && d.K % 256 == 0));
+                                       (d.gs == 32 && d.K % 256 == 0) ||
+                                       (d.gs == 128 && d.K % 1024 == 0));
   void (*fn)(GemmArgs) = nullptr;
   // (kind, x dtype, metadata dtype, two groups per 64-column step)
 #define QP_GEMM_FLAGS(KD, MB, G)                                                 \
@@ -1406,8 +1429,12 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   if (n224 && mch) fn = xb ? k_gemm224<KD, true, MB, G, GSZ> : k_gemm224<KD, false, MB, G, GSZ>; \
   else { QP_GEMM_FLAGS(KD, MB, G) }
 #define QP_GEMM_AFF(KD)                                                          \
-  if (mb) { if (g32) { QP_GEMM_FLAGS_CH(KD, true, true, 32) } else { QP_GEMM_FLAGS_CH(KD, true, false, 64) } } \
-  else { if (g32) { QP_GEMM_FLAGS_CH(KD, false, true, 32) } else { QP_GEMM_FLAGS_CH(KD, false, false, 64) } }
+  if (mb) { if (g32) { QP_GEMM_FLAGS_CH(KD, true, true, 32) }                    \
+            else if (g128) { QP_GEMM_FLAGS_CH(KD, true, false, 128) }            \
+            else { QP_GEMM_FLAGS_CH(KD, true, false, 64) } }                     \
+  else { if (g32) { QP_GEMM_FLAGS_CH(KD, false, true, 32) }                      \
+         else if (g128) { QP_GEMM_FLAGS_CH(KD, false, false, 128) }              \
+         else { QP_GEMM_FLAGS_CH(KD, false, false, 64) } }
   if (d.fmt == AFFINE) {
     if (d.bits == 2) { QP_GEMM_AFF(G_AFF2) }
     else if (d.bits == 4) { QP_GEMM_AFF(G_AFF4) }

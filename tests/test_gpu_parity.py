@@ -186,12 +186,13 @@ def test_gemv_mfma_large_k(q, fmt):
                       f16_weights=True)
 
 
-@pytest.mark.parametrize("fmt", ["affine64", "affine32", "q4k", "q6k", "sym4"])
+@pytest.mark.parametrize("fmt", ["affine64", "affine32", "affine128", "q4k", "q6k", "sym4"])
 def test_gemm_large_k(q, fmt):
     """K = 32768 (512 steps): the qGEMM's metadata chunk rings and staged
     activation offsets cycle many times; both tilings, fp16-weight bound."""
     N, K, M = 300, 32768, 40
     d = {"affine64": q.QDesc.affine(N, K, 4, 64, "bf16"), "affine32": q.QDesc.affine(N, K, 4, 32),
+         "affine128": q.QDesc.affine(N, K, 8, 128, "f16"),
          "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K)}[fmt]
     for ws in ("auto", None):
         print("gemm large K", _id(d), M, ws, flush=True)
