@@ -673,7 +673,7 @@ k_gemm224(GemmArgs a) {
   auto ld_chunk = [&](int c, uint4 (&dst)[2]) {
     dst[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            r.s, r.so + 16u * (uint32_t)c, 0, 0));
-    if constexpr (KIND != G_Q6K)   // Q6K has no second array
+    if constexpr (KIND != G_Q6K && KIND != G_SYM4)   // one array only
       dst[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                              r.z, r.zo + 16u * (uint32_t)c, 0, 0));
   };
@@ -692,7 +692,9 @@ k_gemm224(GemmArgs a) {
   constexpr bool STEPW = KIND == G_Q4K || KIND == G_Q6K;   // step words in ms
   // raw metadata of step t (t % 16 == tu) into a stage: group t (group size
   // 64) or 2t + half (group size 32, Q4K) of the thread's row
-  constexpr int MP = ((MCH == 32 && KIND != G_Q4K) || KIND == G_Q6K) ? 4 : 8;   // steps per chunk
+  // steps per chunk (group-wise SYM4: 4 fp32 scales per chunk)
+  constexpr int MP = KIND == G_SYM4 ? (MCH > 1 ? MCH / 16 : 8)
+                     : ((MCH == 32 && KIND != G_Q4K) || KIND == G_Q6K) ? 4 : 8;
   const uint32_t msh = (KIND == G_Q4K ? 8u : 16u) * (uint32_t)(tid & 1);
   // group size 128: one chunk per 16 steps, i.e. per unrolled iteration;
   // mc[0] holds the current chunk, mc[1] the next (NEXT: step 16 it + 16,
@@ -700,14 +702,17 @@ k_gemm224(GemmArgs a) {
   auto set_meta = [&](auto TU, Stage<KIND>& st, bool next = false) {
     constexpr int tu = decltype(TU)::value;
     constexpr int slot = (tu / MP) & 1;
-    if constexpr (MCH == 128) {
+    if constexpr (MCH == 128 && KIND != G_SYM4) {
       constexpr int e = tu >> 1;   // group of step tu within the chunk
       const uint4& c0 = next ? mc[1][0] : mc[0][0];
       const uint4& c1 = next ? mc[1][1] : mc[0][1];
       st.s0 = (c0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
       st.s1 = (c1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
     } else if constexpr (KIND == G_SYM4) {
-      st.s0 = ms[0];
+      if constexpr (MCH == 1) st.s0 = ms[0];                      // per channel
+      else if constexpr (MCH == 32) st.s0 = mc[slot][0][2 * (tu & 1) + (int)(tid & 1)];
+      else if constexpr (MCH == 64) st.s0 = mc[slot][0][tu & 3];
+      else st.s0 = mc[slot][0][(tu & 7) >> 1];
     } else if constexpr (KIND == G_Q6K) {
       st.s0 = (mc[slot][0][tu & 3] >> msh) & 0xFFFFu;
       st.s2 = ms[(tu >> 2) & 1];
@@ -754,11 +759,12 @@ k_gemm224(GemmArgs a) {
     if constexpr (MCH) {
       // where chunk c' starts (step MP c') load chunk c' + 1 into the slot
       // that chunk c' - 1 held: its last step was converted already
-      if constexpr (MCH == 128) {
+      if constexpr (MCH == 128 && KIND != G_SYM4) {
         if constexpr (u == 0) ld_chunk(kt / 16 + 1, mc[1]);
         set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt, u == 15);
       } else {
-        if constexpr (KIND != G_SYM4 && u % MP == 0) ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
+        if constexpr ((KIND != G_SYM4 || MCH > 1) && u % MP == 0)
+          ld_chunk(kt / MP + 1, mc[((u / MP) + 1) & 1]);
         // step words: super-block b' + 1 at step 4b' (same argument)
         if constexpr (STEPW && u % 4 == 0) ld_step(kt / 4 + 1, ms[((u >> 2) + 1) & 1]);
         set_meta(std::integral_constant<int, (u + 1) & 15>{}, nxt);
@@ -819,9 +825,9 @@ k_gemm224(GemmArgs a) {
   load_stage<KIND, GS32, false, !MCH>(a, r, 0, st0);
   load_stage<KIND, GS32, false, !MCH>(a, r, 1, st1);
   if constexpr (MCH) {
-    if constexpr (KIND == G_SYM4) {
+    if constexpr (KIND == G_SYM4 && MCH == 1) {
       ms[0] = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so, 0, 0);
-    } else if constexpr (MCH == 128) {
+    } else if constexpr (MCH == 128 && KIND != G_SYM4) {
       ld_chunk(0, mc[0]);   // mc[1] is loaded by the first step
     } else {
       ld_chunk(0, mc[0]);
@@ -849,7 +855,7 @@ k_gemm224(GemmArgs a) {
           else kstep(U, kt + u, st1, st0);
         }
       });
-      if constexpr (MCH == 128) {   // the next chunk becomes the current one
+      if constexpr (MCH == 128 && KIND != G_SYM4) {   // the next chunk becomes the current one
         mc[0][0] = mc[1][0];
         mc[0][1] = mc[1][1];
       }
@@ -1450,6 +1456,12 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   } else {
     if (n224 && d.gs == d.K)   // per-channel scale
       fn = xb ? k_gemm224<G_SYM4, true, false, false, 1> : k_gemm224<G_SYM4, false, false, false, 1>;
+    else if (n224 && d.gs == 32 && d.K % 128 == 0)   // group-wise: 4 scales per chunk
+      fn = xb ? k_gemm224<G_SYM4, true, false, true, 32> : k_gemm224<G_SYM4, false, false, true, 32>;
+    else if (n224 && d.gs == 64 && d.K % 256 == 0)
+      fn = xb ? k_gemm224<G_SYM4, true, false, false, 64> : k_gemm224<G_SYM4, false, false, false, 64>;
+    else if (n224 && d.gs == 128 && d.K % 512 == 0)
+      fn = xb ? k_gemm224<G_SYM4, true, false, false, 128> : k_gemm224<G_SYM4, false, false, false, 128>;
     else if (g32) { QP_GEMM_FLAGS(G_SYM4, false, true) } else { QP_GEMM_FLAGS(G_SYM4, false, false) }
   }
 #undef QP_GEMM_AFF

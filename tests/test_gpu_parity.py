@@ -186,14 +186,27 @@ def test_gemv_mfma_large_k(q, fmt):
                       f16_weights=True)
 
 
-@pytest.mark.parametrize("fmt", ["affine64", "affine32", "affine128", "q4k", "q6k", "sym4"])
+@pytest.mark.parametrize("gs", [32, 128])
+@pytest.mark.parametrize("N,K,M", [(130, 512, 9), (257, 1536, 300)])
+def test_gemm_sym4_group_sizes(q, gs, N, K, M):
+    """Group-wise SYM4 group sizes outside the common descriptor list."""
+    d = q.QDesc.sym4(N, K, gs)
+    for ws in ("auto", None):
+        print("gemm sym4", _id(d), M, ws, flush=True)
+        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMM, seed=gs + M, with_bias=True,
+                      workspace=ws)
+
+
+@pytest.mark.parametrize("fmt", ["affine64", "affine32", "affine128", "q4k", "q6k", "sym4",
+                                 "sym4g32", "sym4g128"])
 def test_gemm_large_k(q, fmt):
     """K = 32768 (512 steps): the qGEMM's metadata chunk rings and staged
     activation offsets cycle many times; both tilings, fp16-weight bound."""
     N, K, M = 300, 32768, 40
     d = {"affine64": q.QDesc.affine(N, K, 4, 64, "bf16"), "affine32": q.QDesc.affine(N, K, 4, 32),
          "affine128": q.QDesc.affine(N, K, 8, 128, "f16"),
-         "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K)}[fmt]
+         "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K),
+         "sym4g32": q.QDesc.sym4(N, K, 32), "sym4g128": q.QDesc.sym4(N, K, 128)}[fmt]
     for ws in ("auto", None):
         print("gemm large K", _id(d), M, ws, flush=True)
         _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMM, seed=3, with_bias=True,
