@@ -21,8 +21,3 @@ def linear_f64(x64, qz, f: QFormat, bias64=None, w64=None):
         y = y + np.asarray(bias64, np.float64)[None, :]
     return y
 
-
-def linear_rows_f64(x64, qz_rows, f: QFormat, bias64=None):
-    """Same as linear_f64, for a subset of output rows whose codes and
-    metadata were sliced beforehand (rows are independent)."""
-    return linear_f64(x64, qz_rows, f, bias64)

@@ -142,7 +142,7 @@ def test_other_entry_points_validate(q):
 def test_workspace_query_and_checks(q):
     n = ctypes.c_size_t(7)
     d = q.QDesc.affine(64, 512).c()
-    # qGEMM: M rounded up to 32 rows of K fp16; other kernels take none
+    # qGEMM: M rounded up to 16 rows of K fp16; other kernels take none
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 300, 2, ctypes.byref(n)) == q.QP_OK
     assert n.value == 304 * 512 * 2
     # 8192 rows at M = 2048: 256 blocks of 256 rows (one wave) beat 296

@@ -44,6 +44,8 @@ def _codes_rule(case):
         return (k % 16)[None, :]
     if rule == "code at k = 5":
         return np.full((1, K), 5)
+    if rule == "code at k = 15":
+        return np.full((1, K), 15)
     if rule == "code at k = (k % 63) - 31":
         return ((k % 63) - 31)[None, :]
     raise KeyError(rule)
@@ -136,7 +138,9 @@ def test_quantize_golden(case):
     qz = oracle.quantize(W, f)
     assert qz["codes"][0].astype(int).tolist() == q.tolist()
     assert np.all(qz["sc"] == case["sc_all"])
-    assert np.all(Fraction(float(s)) == Fraction(case["s_all"]) for s in qz["s"][0])
+    assert all(Fraction(float(v)) == Fraction(case["s_all"]) for v in qz["s"][0])
+    if "z_all" in case:
+        assert all(Fraction(float(v)) == Fraction(case["z_all"]) for v in qz["z"][0])
     w = oracle.dequant_f64(qz, f)[0]
     if case["fmt"] == "q4k":
         assert np.all(qz["zc"] == case["zc_all"])
@@ -149,6 +153,73 @@ def test_quantize_golden(case):
         assert qz["step"].view(np.uint16).tolist() == [[case["step_bits"]]]
         for k in range(256):
             assert Fraction(float(w[k])) == int(q[k]) * Fraction(127 * 129, 1 << 20)
+
+
+def _q4k_qz(case):
+    return {"codes": _codes_rule(case).astype(np.uint8),
+            "sc": np.array(case["sc"], np.uint8),
+            "zc": np.array(case["zc"], np.uint8),
+            "sstep": np.array(case["sstep_bits"], np.uint16).view(np.float16),
+            "zstep": np.array(case["zstep_bits"], np.uint16).view(np.float16)}
+
+
+@pytest.mark.parametrize("case", GOLD["dequant_f32_order"], ids=lambda c: c["name"][:30])
+def test_dequant_f32_operation_order(case):
+    """The fp32 dequantization evaluates (q - zero) * scale in the page's
+    order, one IEEE fp32 operation each: where q - zero is inexact this can
+    differ by one unit in the last place from the exact value rounded once
+    (hand-worked case)."""
+    f = QFormat.q4k()
+    qz = _q4k_qz(case)
+    k = case["k"]
+    w = oracle.dequant_f64(qz, f)
+    assert Fraction(float(w[0, k])) == Fraction(case["exact"])
+    w32 = oracle.dequant_f32(qz, f)
+    assert Fraction(float(w32[0, k])) == Fraction(case["f32_in_order"])
+    # the two readings really differ here
+    assert Fraction(float(np.float32(w[0, k]))) == Fraction(case["f32_rounded_once"])
+    assert case["f32_in_order"] != case["f32_rounded_once"]
+    # dequant_out('f32') is that same fp32 evaluation
+    assert np.array_equal(oracle.dequant_out(qz, f, "f32"), w32)
+
+
+# ------------------------------------------------------------ bf16 rounding
+@pytest.mark.parametrize("case", GOLD["bf16_rne"], ids=lambda c: c["f32"])
+def test_bf16_rne_golden(case):
+    x = np.array([int(case["f32"], 16)], np.uint32).view(np.float32)
+    assert oracle.f32_to_bf16_bits(x).tolist() == [int(case["bf16"], 16)]
+    # widening back is exact
+    b = np.array([int(case["bf16"], 16)], np.uint16)
+    assert oracle.bf16_bits_to_f32(b).view(np.uint32).tolist() == [int(case["bf16"], 16) << 16]
+
+
+def test_bf16_rne_matches_torch():
+    """Against an independent implementation: torch's CPU fp32 -> bfloat16
+    conversion (round to nearest, ties to even) on 10^6 random finite bit
+    patterns plus every upper half combined with the lower halves around a
+    tie (0x7FFF, 0x8000, 0x8001) and 0."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    u = rng.integers(0, 2**32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    adv = (hi[:, None] | np.array([0x0000, 0x7FFF, 0x8000, 0x8001], np.uint32)[None, :]).ravel()
+    u = np.concatenate([u, adv])
+    u = u[(u & 0x7F800000) != 0x7F800000]          # finite inputs only
+    x = u.view(np.float32)
+    got = oracle.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------------- SNR
+@pytest.mark.parametrize("case", GOLD["snr_db"], ids=lambda c: c["name"][:20])
+def test_snr_db_golden(case):
+    ref = np.array(case["ref"])
+    approx = np.array(case["approx"])
+    assert oracle.snr_db(ref, approx) == pytest.approx(case["db"], abs=1e-12)
+    # scale invariant, and symmetric in the sign of the error
+    assert oracle.snr_db(4 * ref, 4 * approx) == pytest.approx(case["db"], abs=1e-12)
+    assert oracle.snr_db(ref, 2 * ref - approx) == pytest.approx(case["db"], abs=1e-12)
 
 
 # ------------------------------------------------------------- P-roundtrip
