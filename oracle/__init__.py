@@ -20,7 +20,8 @@ Sources (the pages this follows):
     codes stay identical to the source values, only metadata is re-quantized.
     Review comment 1: max-based step, codes clamped to [0, 255], zero >= 0.
   * ExecuTorch PR #16577 "Arm backend: Support a8w4", description: int4
-    carried in an int8 with qmin=-7, qmax=7.
+    carried in an int8 with qmin=-7, qmax=7; int8 activations (a8w4.py, with
+    the per-token activation rule it states as a reading).
 
 Every floating-point operation that the format fixes is done in IEEE fp32
 (NumPy float32 arithmetic is correctly rounded), ties round half to even,
@@ -44,6 +45,7 @@ from .dequant import dequant_f64, dequant_f32, dequant_out
 from .linear import linear_f64
 from .sizes import buffer_bytes, bits_per_weight
 from .metrics import snr_db, rel_l2, maxabs_bound
+from .a8w4 import quantize_activations, dequantize_activations, linear_a8w4
 
 __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "f16_bits_to_f32",
@@ -51,4 +53,5 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_bits", "unpack_bits", "dequant_f64",
     "dequant_f32", "dequant_out", "linear_f64", "buffer_bytes",
     "bits_per_weight", "snr_db", "rel_l2", "maxabs_bound",
+    "quantize_activations", "dequantize_activations", "linear_a8w4",
 ]
