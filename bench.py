@@ -168,11 +168,83 @@ def gemm_case(q, desc, W_np, x_bits, steps, warmup, warmup_s=0.3):
                 frac=tf / MFMA_F16_PEAK_TFLOPS, tok_s_per_layer=M / per)
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:
+        return 1
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    r = fn()
+    return r, time.perf_counter() - t0
+
+
+def cpu_stages(rows=2048):
+    """The oracle's stages timed separately for every workload: quantize,
+    pack into the device buffers, fp64 dequantize and the fp64 matmul, on
+    the first `rows` weight rows of each layer (seed 0), scaled to the whole
+    layer; plus one whole-layer decode forward (dequantize + matvec) of the
+    int4 affine decode layer on a single core."""
+    import numpy as np
+    import oracle
+    from oracle import QFormat
+    from oracle.packing import to_buffers
+    from bit_weight_only_qlinear_amd import synth
+    cases = [("tiny_w4a16", "int4 affine gs64 fp16 meta", QFormat.affine(4, 64, "f16"), "f16"),
+             ("decode_affine", "int4 affine gs64", QFormat.affine(4, 64, "bf16"), "bf16"),
+             ("decode_affine", "int2 affine gs64", QFormat.affine(2, 64, "bf16"), "bf16"),
+             ("decode_affine", "int8 affine gs64", QFormat.affine(8, 64, "bf16"), "bf16"),
+             ("decode_q4k", "Q4_K-style", QFormat.q4k(), "bf16"),
+             ("decode_8k", "Q6_K-style", QFormat.q6k(), "bf16"),
+             ("decode_8k", "sym int4 per-channel", QFormat.sym4(8192), "bf16"),
+             ("prefill_affine", "int4 affine gs64", QFormat.affine(4, 64, "bf16"), "bf16")]
+    out = []
+    wl_cache = {}
+    for name, label, f, xdt in cases:
+        if name not in wl_cache:
+            wl_cache.clear()
+            wl_cache[name] = synth.make(name, seed=0, M=8 if name == "decode_8k" else None)
+        wl = wl_cache[name]
+        N, K = wl.W.shape
+        r = min(rows, N)
+        Ws = wl.W[:r]
+        x64 = oracle.decode_activations(wl.x_bits, xdt)
+        qz, tq = _timed(lambda: oracle.quantize(Ws, f))
+        _, tp = _timed(lambda: to_buffers(qz, f))
+        w64, td = _timed(lambda: oracle.dequant_f64(qz, f))
+        _, tm = _timed(lambda: np.matmul(x64, w64.T))
+        sc = N / r
+        out.append({"workload": f"{name}: {label}, M={x64.shape[0]} K={K} N={N}",
+                    "sample_rows": r,
+                    "quantize_s": round(tq * sc, 4), "pack_s": round(tp * sc, 4),
+                    "dequant_s": round(td * sc, 4), "matmul_s": round(tm * sc, 5)})
+        log("cpu", out[-1])
+    wl_cache.clear()
+    # whole decode layer, int4 affine, one core
+    wl = synth.make("decode_affine", seed=0)
+    f = QFormat.affine(4, 64, "bf16")
+    qz = oracle.quantize(wl.W, f)
+    x64 = oracle.decode_activations(wl.x_bits, "bf16")
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            _, t1 = _timed(lambda: oracle.linear_f64(x64, qz, f))
+        single = {"workload": "decode_affine: int4 affine gs64, M=1 K=4096 N=14336, whole "
+                              "layer (fp64 dequantize + matvec)", "cores": 1,
+                  "forward_s": round(t1, 4)}
+    except ImportError:
+        single = None
+    return out, single
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle (NumPy, fp64 dequant + matvec) on the headline workload:
     whole-layer forwards of K=4096, N=14336 int4 affine, repeated until the
-    time budget is spent (at least one)."""
-    import numpy as np
+    time budget is spent (at least one); then the per-stage times of every
+    workload."""
     import oracle
     from oracle import QFormat
     from bit_weight_only_qlinear_amd import synth
@@ -182,11 +254,7 @@ def cpu_baseline(budget_s=12.0):
     x64 = oracle.decode_activations(wl.x_bits, "bf16")
     N, K = wl.W.shape
     nbytes = N * K // 2 + 2 * N * (K // 64) * 2 + K * 2 + N * 2
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
-    except Exception:
-        threads = 1
+    threads = _blas_threads()
     calls = 0
     t0 = time.perf_counter()
     while True:
@@ -195,11 +263,19 @@ def cpu_baseline(budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    del wl, qz
+    stages, single = cpu_stages()
     return {"value": round(nbytes * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "host_cpu_count": os.cpu_count(),
             "kind": "oracle",
             "sample": f"{calls} whole-layer forwards (fp64 dequantize + matvec) of "
                       f"M=1, K=4096, N=14336 int4 affine gs64 in {el:.1f} s; "
-                      f"elementwise NumPy on 1 thread, BLAS on {threads}"}
+                      f"elementwise NumPy on 1 thread, BLAS on {threads}",
+            "stages": stages,
+            "stages_note": "per workload: the oracle's quantize, pack, fp64 dequantize and "
+                           "fp64 matmul timed once on the first 2048 weight rows (seed 0) "
+                           "and scaled to the whole layer",
+            "single_core": single}
 
 
 def main():

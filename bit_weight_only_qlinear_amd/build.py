@@ -25,6 +25,8 @@ SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
     "gemm.hip": [],
+    "skinny.hip": [],
+    "a8w4.hip": [],
 }
 
 

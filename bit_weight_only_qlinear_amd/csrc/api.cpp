@@ -160,9 +160,13 @@ qp_status hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-// The qGEMM addresses a block's 256 activation rows through a 32-bit buffer
-// resource (256 * K * 2 bytes), hence K <= 2^22.
-bool gemm_ok(const qp::Desc& d) { return d.K % 64 == 0 && d.K <= (int64_t(1) << 22); }
+// The qGEMM rounds each dequantized weight once to fp16 (relative error up
+// to 2^-11).  That error grows like sqrt(K) against the layer's element
+// bound 1e-2 * ||x|| * max|w| / sqrt(K); the kernel is held to the bound up
+// to K = 8192 (the largest K of the workloads it is verified on), and longer
+// rows take the exact-code MFMA kernel instead.
+constexpr int64_t kGemmMaxK = 8192;
+bool gemm_ok(const qp::Desc& d) { return d.K % 64 == 0 && d.K <= kGemmMaxK; }
 
 }  // namespace
 
@@ -255,37 +259,38 @@ qp_status plan_forward(const qp_desc* d, qp::Desc* dd, int32_t x_dtype, int64_t 
       kernel != QP_KERNEL_GEMV_MFMA)
     return fail(QP_EINVAL, "unknown kernel selector %d", kernel);
   if (kernel == QP_KERNEL_GEMM && !gemm_ok(*dd))
-    return fail(QP_EUNSUPPORTED, "the qGEMM kernel needs K %% 64 == 0 and K <= 2^22 (K=%lld)",
-                (long long)dd->K);
+    return fail(QP_EUNSUPPORTED,
+                "the qGEMM kernel (fp16-rounded weights) needs K %% 64 == 0 and K <= %lld, "
+                "where it meets the output bound (K=%lld); QP_KERNEL_AUTO and "
+                "QP_KERNEL_GEMV_MFMA use exact codes at any K",
+                (long long)kGemmMaxK, (long long)dd->K);
   sizes_of(*dd, nbytes);
   bool small_bufs = (size_t)M * (size_t)dd->K * 2 < (size_t(1) << 31);
   for (int i = 0; i < 5; ++i) small_bufs = small_bufs && nbytes[i] < (size_t(1) << 31);
   const bool gemv_fits = qp::gemv_supported(*dd) && small_bufs;
-  const bool skinny_fits = qp::skinny_supported(*dd) && M <= 16 && small_bufs;
+  const bool skinny_fits = qp::skinny_supported(*dd) && small_bufs;
   if (kernel == QP_KERNEL_GEMV && !gemv_fits)
     return fail(QP_EUNSUPPORTED,
                 "the qGEMV kernel needs K <= its register plan (K=%lld) and every buffer < 2 GiB",
                 (long long)dd->K);
   if (kernel == QP_KERNEL_GEMV_MFMA && !skinny_fits)
     return fail(QP_EUNSUPPORTED,
-                "the MFMA qGEMV kernel needs M <= 16, K %% 128 == 0 and every buffer < 2 GiB "
-                "(M=%lld, K=%lld)",
-                (long long)M, (long long)dd->K);
+                "the MFMA qGEMV kernel needs K %% 128 == 0 and every buffer < 2 GiB (K=%lld)",
+                (long long)dd->K);
   if (kernel == QP_KERNEL_AUTO) {
-    // The MFMA qGEMV dequantizes each weight once instead of doing one dot
-    // product per activation row.  Where it takes over (measured on
-    // 8192 x 8192 layers): 2 rows for per-channel SYM4 (exact codes), 4 for
-    // Q6K (costly 6-bit dequantization), 3 for the others.
+    // The MFMA qGEMV runs one set of MFMAs per 16 activation rows instead of
+    // one dot product per row and code pair.  Where it takes over from the
+    // streaming qGEMV (timed on 8192 x 8192 layers): 2 rows for per-channel
+    // SYM4, 4 for Q6K, 3 for the others.  Past 16 rows the qGEMM, up to the
+    // K where its fp16 weights hold the output bound; beyond that the exact
+    // MFMA qGEMV in tiles of 16 activation rows.
     int64_t mfma_from = 3;
     if (dd->fmt == qp::SYM4 && dd->gs == dd->K) mfma_from = 2;
     else if (dd->fmt == qp::Q6K) mfma_from = 4;
-    // fp16-rounded weights add an error that grows like sqrt(K) against the
-    // layer's element bound; past K = 16384 small M stays on the exact-code
-    // qGEMV
-    const bool exact_preferred = dd->K > 16384 && M <= 8 && gemv_fits;
-    if (M >= mfma_from && M <= 16 && skinny_fits && !exact_preferred) *use = USE_SKINNY;
+    if (M >= mfma_from && M <= 16 && skinny_fits) *use = USE_SKINNY;
     else if (M <= 8 && gemv_fits) *use = USE_GEMV;
     else if (gemm_ok(*dd)) *use = USE_GEMM;
+    else if (skinny_fits) *use = USE_SKINNY;
     else if (gemv_fits) *use = USE_GEMV;
     else return fail(QP_EUNSUPPORTED, "no kernel supports K=%lld for this format", (long long)dd->K);
   } else {
@@ -368,6 +373,55 @@ qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype, int6
                           const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
                           void* stream) {
   return qlinear_forward_kernel(d, x, x_dtype, M, w, bias, y, y_dtype, QP_KERNEL_AUTO, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+qp_status qpack_quantize_activations(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                     void* xq, float* xs, void* stream) {
+  if (x_dtype != QP_F16 && x_dtype != QP_BF16)
+    return fail(QP_EINVAL, "x_dtype must be QP_F16 or QP_BF16 (got %d)", x_dtype);
+  if (M <= 0 || K <= 0)
+    return fail(QP_ESHAPE, "M and K must be positive (M=%lld, K=%lld)", (long long)M, (long long)K);
+  if (M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 24))
+    return fail(QP_EUNSUPPORTED, "M must be < 2^31 and K <= 2^24 (M=%lld, K=%lld)", (long long)M,
+                (long long)K);
+  if (!x || !xq || !xs) return fail(QP_EINVAL, "x, xq and xs must not be NULL");
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(xs))
+    return fail(QP_EALIGN, "x, xq and xs must be 16-byte aligned");
+  (void)hipGetLastError();
+  return hip_status(qp::launch_quant_act(x, x_dtype, M, K, xq, xs, (hipStream_t)stream),
+                    "qpack_quantize_activations launch");
+}
+
+qp_status qlinear_forward_a8w4(const qp_desc* d, const void* xq, const float* xs, int64_t M,
+                               const qp_weights* w, const float* bias, void* y, int32_t y_dtype,
+                               void* stream) {
+  qp::Desc dd;
+  qp_status st = check_desc(d, &dd);
+  if (st != QP_OK) return st;
+  if (dd.fmt != qp::SYM4 || dd.gs != dd.K)
+    return fail(QP_EUNSUPPORTED,
+                "a8w4 takes the SYM4 format with one scale per output channel (group_size = K)");
+  if (dd.K % 128)
+    return fail(QP_ESHAPE, "a8w4 needs K %% 128 == 0 (K=%lld)", (long long)dd.K);
+  if (M <= 0) return fail(QP_ESHAPE, "M must be positive (got %lld)", (long long)M);
+  if ((uint64_t)M * (uint64_t)dd.K >= (uint64_t(1) << 31) ||
+      (uint64_t)dd.N * (uint64_t)dd.K / 2 >= (uint64_t(1) << 31))
+    return fail(QP_EUNSUPPORTED, "a8w4 needs the activations and the codes each < 2 GiB");
+  if ((st = check_weights(dd, w, false)) != QP_OK) return st;
+  if (y_dtype != QP_F16 && y_dtype != QP_BF16 && y_dtype != QP_F32)
+    return fail(QP_EINVAL, "y_dtype must be QP_F16, QP_BF16 or QP_F32 (got %d)", y_dtype);
+  if (!xq || !xs || !y) return fail(QP_EINVAL, "xq, xs and y must not be NULL");
+  if (!aligned16(xq) || !aligned16(xs) || !aligned16(y))
+    return fail(QP_EALIGN, "xq, xs and y must be 16-byte aligned");
+  if (bias && !aligned16(bias)) return fail(QP_EALIGN, "bias is not 16-byte aligned");
+  (void)hipGetLastError();
+  return hip_status(qp::launch_a8w4(dd, xq, xs, M, bufs_of(w), bias, y, y_dtype,
+                                    (hipStream_t)stream),
+                    "qlinear_forward_a8w4 launch");
 }
 
 }  // extern "C"

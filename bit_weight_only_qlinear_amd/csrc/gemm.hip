@@ -6,9 +6,10 @@
 // dequantizes its weight tile on the way into LDS.  The tile is rounded once
 // to fp16 rather than bf16: bf16 keeps 8 significant bits, which is not
 // enough for the output tolerance of this layer, fp16 keeps 11, and gfx950
-// runs fp16 and bf16 MFMA at the same rate.  Activations are converted from
-// bf16 to fp16 in the same staging step (exact for magnitudes in
-// [2^-17, 65504]).
+// runs fp16 and bf16 MFMA at the same rate.  bf16 activations are converted
+// to fp16 in the same staging step after an exact power-of-two prescale per
+// row (k_xexp) that puts the row's peak in [2^14, 2^15), so any finite bf16
+// row fits fp16's range; the fp32 epilogue undoes the scale.
 //
 // Design:
 //  * Block tile 256 (n) x 256 (m) x 64 (k), 8 waves in a 2 (n) x 4 (m)
@@ -97,6 +98,15 @@ struct GemmArgs {
   int64_t M, N, K;
   int gs, ydt, tilesM, tilesN;
 };
+
+// Prescale exponent of activation row m, as the exponent kernel left it in
+// y at (m, c): the first column of each n-tile of the row.  Only the block
+// of that tile reads it, before it writes the tile.
+__device__ __forceinline__ int read_exp(const GemmArgs& a, int64_t m, int64_t c) {
+  const int64_t i = m * a.N + c;
+  return a.ydt == F32 ? static_cast<const int*>(a.y)[i]
+                      : (int)(int16_t) static_cast<const uint16_t*>(a.y)[i];
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
@@ -270,14 +280,17 @@ __device__ __forceinline__ uint4 weight_chunk(const Stage<KIND>& st, int j, uint
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-// 8 activations (raw bits) as fp16 in the order (0,4,1,5,2,6,3,7).
+// 8 activations (raw bits) as fp16 in the order (0,4,1,5,2,6,3,7); bf16
+// activations are first scaled by 2^e, the row's prescale exponent (exact),
+// which brings the row's largest magnitude into [2^14, 2^15).
 template <bool XBF16>
-__device__ __forceinline__ uint4 act_chunk(const uint4 u) {
+__device__ __forceinline__ uint4 act_chunk(const uint4 u, int e = 0) {
   if constexpr (XBF16) {
-    // bf16 -> fp32 is a shift; fp32 -> fp16 is exact in range, so the
-    // rounding mode of the packed conversion does not matter
-    auto lo = [](uint32_t v) { return __uint_as_float(v << 16); };
-    auto hi = [](uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); };
+    // bf16 -> fp32 is a shift, the scaling exact; fp32 -> fp16 is exact for
+    // magnitudes within 2^-10 .. 2^31 of the row's largest (everything a
+    // bf16's 8 significant bits can hold there), smaller ones round
+    auto lo = [e](uint32_t v) { return ldexpf(__uint_as_float(v << 16), e); };
+    auto hi = [e](uint32_t v) { return ldexpf(__uint_as_float(v & 0xFFFF0000u), e); };
     return make_uint4(pack_f16(lo(u.x), lo(u.z)), pack_f16(hi(u.x), hi(u.z)),
                       pack_f16(lo(u.y), lo(u.w)), pack_f16(hi(u.y), hi(u.w)));
   } else {
@@ -301,11 +314,12 @@ __device__ __forceinline__ int wrow_of(int t) {
 // half row.
 template <int KIND, bool XBF16, bool MBF16>
 __device__ __forceinline__ void convert_part(const Stage<KIND>& st, int p, unsigned char* smem,
-                                             uint32_t buf, int tid, uint32_t magic) {
+                                             uint32_t buf, int tid, uint32_t magic, const int* xe) {
   // activation row (tid >> 3) + 64 p: (row >> 1) & 7 == (tid >> 4) & 7
   const uint32_t xb = kXBase + (uint32_t)(tid >> 3) * 128u +
                       (uint32_t)((tid & 7) ^ ((tid >> 4) & 7)) * 16u;
-  *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 8192u * p)) = act_chunk<XBF16>(st.x[p]);
+  *reinterpret_cast<uint4*>(smem + xb + (buf * kTileBytes + 8192u * p)) =
+      act_chunk<XBF16>(st.x[p], XBF16 ? xe[(tid >> 3) + 64 * p] : 0);
   const int n = wrow_of(tid), j = 4 * (tid & 1) + p;
   const uint32_t wb = (uint32_t)n * 128u + (uint32_t)((j ^ ((n >> 1) & 7)) * 16);
   *reinterpret_cast<uint4*>(smem + wb + buf * kTileBytes) = weight_chunk<KIND, MBF16>(st, p, magic);
@@ -351,6 +365,7 @@ template <int KIND, bool XBF16, bool MBF16, bool GS32>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kTileBytes];
+  __shared__ int s_xe[BM];   // prescale exponents of the block's activation rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -446,7 +461,7 @@ k_gemm(GemmArgs a) {
         B[0] = Bn[0];
         B[1] = Bn[1];
       }
-      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic);
+      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic, s_xe);
 #if QP_GEMM_SGB
       // instruction order of the slice: B prefetch, then per A fragment two
       // MFMAs, its re-read and a share of the conversion
@@ -479,7 +494,7 @@ k_gemm(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic);
+      convert_part<KIND, XBF16, MBF16>(nxt, s, smem, cur ^ 1u, tid, magic, s_xe);
     }
 #endif
     __syncthreads();
@@ -488,8 +503,12 @@ k_gemm(GemmArgs a) {
   Stage<KIND> st0, st1;
   load_stage<KIND, GS32>(a, r, 0, st0);
   load_stage<KIND, GS32>(a, r, 1, st1);
+  if constexpr (XBF16) {
+    if (tid < BM) s_xe[tid] = m0 + tid < a.M ? read_exp(a, m0 + tid, n0) : 0;
+    __syncthreads();
+  }
 #pragma unroll
-  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16>(st0, p, smem, 0u, tid, magic);
+  for (int p = 0; p < 4; ++p) convert_part<KIND, XBF16, MBF16>(st0, p, smem, 0u, tid, magic, s_xe);
   __syncthreads();
   for (int kt = 0; kt < KT; kt += 2) {
     kstep(kt, st0, st1);
@@ -525,9 +544,10 @@ k_gemm(GemmArgs a) {
         constexpr int j = decltype(J)::value;
         const int64_t m = m0 + wj * 64 + j * 32 + (el & 31);
         const int64_t idx = m * a.N + n;
+        const int xe = XBF16 ? s_xe[wj * 64 + j * 32 + (el & 31)] : 0;
         float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q] + bv[q];
+        for (int q = 0; q < 4; ++q) v[q] = ldexpf(acc[i][j][4 * g + q], -xe) + bv[q];
         const bool mok = m < a.M;
         if (mok && vec4 && n < a.N) {
           if (ydt == F32) {
@@ -577,18 +597,48 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // of v_mfma_f32_16x16x32_f16.  16-byte chunk c = (mb * K/32 + kq) * 64 + l
 // holds row 16 mb + (l & 15), columns 32 kq + 8 (l >> 4) .. + 7 in the order
 // (0,4,1,5,2,6,3,7); rows from M up to the next multiple of 16 are zero.
+// bf16 rows are prescaled by their exponent (left in y by k_xexp, at the
+// row's column 0).
 template <bool XBF16>
 __global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
                                                uint4* __restrict__ xf, uint32_t M, uint32_t K,
-                                               uint32_t nchunks) {
+                                               uint32_t nchunks, GemmArgs a) {
   const uint32_t c = blockIdx.x * 256u + threadIdx.x;
   if (c >= nchunks) return;
   const uint32_t l = c & 63u, blk = c >> 6, kb = K / 32u;
   const uint32_t mb = blk / kb, kq = blk - mb * kb;
   const uint32_t row = 16u * mb + (l & 15u), col = 32u * kq + 8u * (l >> 4);
   uint4 u = make_uint4(0u, 0u, 0u, 0u);
-  if (row < M) u = *reinterpret_cast<const uint4*>(x + (uint64_t)row * K + col);
-  xf[c] = act_chunk<XBF16>(u);
+  int e = 0;
+  if (row < M) {
+    u = *reinterpret_cast<const uint4*>(x + (uint64_t)row * K + col);
+    if constexpr (XBF16) e = read_exp(a, row, 0);
+  }
+  xf[c] = act_chunk<XBF16>(u, e);
+}
+
+// Prescale exponent of each bf16 activation row: e = 14 - floor(log2 of the
+// row's largest magnitude) (0 for an all-zero row), so that every scaled row
+// peaks in [2^14, 2^15) -- inside fp16's range, with fp16's full precision
+// for everything within 2^-10 of the peak.  Written into y at the first
+// column of every n-tile (tile width `colstep`), where the qGEMM block of
+// that tile picks it up before it writes its outputs.  One block per row.
+__global__ void __launch_bounds__(256) k_xexp(const uint16_t* __restrict__ x, int64_t K, void* y,
+                                              int64_t N, int ydt, int colstep, int ntiles) {
+  __shared__ float wm[4];
+  const int64_t m = blockIdx.x;
+  float mx = 0.f;
+  for (int64_t k = threadIdx.x; k < K; k += 256) mx = fmaxf(mx, fabsf(bf16_to_f32(x[m * K + k])));
+  mx = wave_max_all(mx);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  const int e = mx == 0.f ? 0 : 14 - ilogbf(mx);
+  for (int t = threadIdx.x; t < ntiles; t += 256) {
+    const int64_t i = m * N + (int64_t)t * colstep;
+    if (ydt == F32) static_cast<int*>(y)[i] = e;
+    else static_cast<int16_t*>(y)[i] = (int16_t)e;
+  }
 }
 
 // MCH = group size (affine, 128 with K % 1024 == 0, 64 with K % 512 == 0 or
@@ -603,6 +653,7 @@ template <int KIND, bool XBF16, bool MBF16, bool GS32, int MCH>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_gemm224(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kTileBytes];
+  __shared__ int s_xe[BM];   // prescale exponents of the block's activation rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -845,6 +896,9 @@ k_gemm224(GemmArgs a) {
     for (int j = 0; j < 4; ++j) Bf[sub][j] = ld_b(0, sub, j);
 #pragma unroll
   for (int p = 0; p < 4; ++p) st_w(0u, p, weight_chunk<KIND, MBF16>(st0, p, magic));
+  if constexpr (XBF16) {
+    if (tid < BM) s_xe[tid] = m0 + tid < a.M ? read_exp(a, m0 + tid, n0) : 0;
+  }
   __syncthreads();
   if constexpr (MCH) {
     for (int kt = 0; kt < KT; kt += 16) {
@@ -891,9 +945,10 @@ k_gemm224(GemmArgs a) {
       constexpr int j = decltype(J)::value;
       const int64_t m = m0 + wj * 64 + j * 16 + (el & 15);
       const int64_t idx = m * a.N + n;
+      const int xe = XBF16 ? s_xe[wj * 64 + j * 16 + (el & 15)] : 0;
       float v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = acc[i][j][q] + bv[q];
+      for (int q = 0; q < 4; ++q) v[q] = ldexpf(acc[i][j][q], -xe) + bv[q];
       const bool mok = m < a.M;
       if (mok && vec4 && n < a.N) {
         if (ydt == F32) {
@@ -921,448 +976,7 @@ k_gemm224(GemmArgs a) {
   });
 }
 
-// ===========================================================================
-// Skinny MFMA kernel for decode batches, 4 <= M <= 16 (y = x W^T).
-//
-// With per-row dot products every code pair costs M dot instructions; here
-// each weight is dequantized once (as in the qGEMM) and the M activation
-// rows ride in the 16 columns of v_mfma_f32_16x16x32_f16 (columns past M
-// are zero).  A block owns 32 weight rows (two 16-row MFMA tiles); its 8
-// waves take every 8th 128-column block of K, and their partial sums meet in
-// LDS.  In a 128-column block, lane l (r = l & 15, g = l >> 4) covers
-// columns 32 g .. 32 g + 31 of weight row r of each tile and of activation
-// row r: MFMA step t uses its 8-column chunk t, in the same column order
-// (0,4,1,5,2,6,3,7) on both operands.  Lane l holds D[4 g + v][r] of each
-// 16 x 16 tile (v = 0..3).  Weights are dequantized to fp16 as in the qGEMM,
-// except per-channel SYM4: its codes q = u - 8 are exact in fp16 and the
-// fp32 channel scale multiplies the reduced sum (rounding the scale to fp16
-// would bias every weight of a row the same way).
-// ===========================================================================
-#ifndef QP_SK_WAVES
-#define QP_SK_WAVES 8
-#endif
-#ifndef QP_SK_DEPTH
-#define QP_SK_DEPTH 1
-#endif
-constexpr int kSkRows = 32;             // weight rows per block
-constexpr int kSkWaves = QP_SK_WAVES;   // K splits per block
-constexpr int kSkDepth = QP_SK_DEPTH;   // column blocks in flight ahead of the one computed
-constexpr int kSkCols = 128;    // columns per block step
-
-struct SkinnyArgs {
-  const void* qw;
-  const void* qh;
-  const void* scales;
-  const void* zeros;
-  const void* steps;
-  const void* x;
-  const void* bias;
-  void* y;
-  int64_t M, N, K;
-  int gs, ydt;
-  uint32_t meta_bytes[3];   // scales, zeros, steps: allocated sizes (16-byte multiples)
-  uint32_t lds_meta[3];     // LDS byte offsets of the staged metadata (LM kernels)
-};
-
-// One 128-column block of one lane: codes of its two rows (32 columns
-// each), their metadata, and its activation chunks.
-template <int KIND>
-struct SkStage {
-  int kb;                   // which column block
-  uint4 x[4];
-  uint32_t w[2][GT<KIND>::W / 2];
-  uint32_t h[2][GT<KIND>::H > 0 ? GT<KIND>::H / 2 : 1];
-  uint32_t s0[2], s1[2], s2[2];
-};
-
-// Unsigned field of element e (0..7) of chunk j (0..3) of a lane's 32 columns.
-template <int KIND>
-__device__ __forceinline__ uint32_t sk_field(const uint32_t* w, const uint32_t* h, int j, int e) {
-  if constexpr (KIND == G_AFF2) return (w[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u;
-  else if constexpr (KIND == G_AFF8) return (w[2 * j + (e >> 2)] >> (8 * (e & 3))) & 255u;
-  else if constexpr (KIND == G_Q6K)
-    return ((w[j] >> (4 * e)) & 15u) | (((h[j >> 1] >> (2 * (8 * (j & 1) + e))) & 3u) << 4);
-  else return (w[j] >> (4 * e)) & 15u;
-}
-
-template <int KIND, bool MBF16, bool PERCH>
-__device__ __forceinline__ half8_t sk_weight_frag(const SkStage<KIND>& st, int i, int j,
-                                                  uint32_t magic) {
-  if constexpr (PERCH) {
-    // SYM4 with one fp32 scale per output channel: the MFMA takes the exact
-    // codes q = u - 8 (fp16 1024 + u minus 1032) and the scale is applied
-    // once per output in fp32
-    uint32_t p[4];
-    const half2_t off = {(_Float16)1032.f, (_Float16)1032.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p[e] = __builtin_bit_cast(
-          uint32_t, __builtin_bit_cast(half2_t, and_or(st.w[i][j] >> (4 * e), 0x000F000Fu, magic)) - off);
-    return __builtin_bit_cast(half8_t, make_uint4(p[0], p[1], p[2], p[3]));
-  }
-  float S, T;
-  if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
-    const uint32_t sb = st.s0[i] & 0xFFFFu, tb = st.s1[i] & 0xFFFFu;
-    S = MBF16 ? bf16_to_f32(sb) : f16_to_f32(sb);
-    T = MBF16 ? bf16_to_f32(tb) : f16_to_f32(tb);
-  } else if constexpr (KIND == G_Q4K) {
-    S = (float)(st.s0[i] & 0xFFu) * f16_to_f32(st.s2[i] & 0xFFFFu);
-    T = -S * ((float)(st.s1[i] & 0xFFu) * f16_to_f32(st.s2[i] >> 16));
-  } else if constexpr (KIND == G_Q6K) {
-    S = (float)(int8_t)((st.s0[i] >> (8 * (j >> 1))) & 0xFFu) * f16_to_f32(st.s2[i] & 0xFFFFu);
-    T = -32.f * S;
-  } else {
-    S = __uint_as_float(st.s0[i]);
-    T = -8.f * S;
-  }
-  uint32_t p[4];
-  if constexpr (KIND == G_AFF4) {
-    // fp16 pairs of the codes, one packed fma: exact codes, one rounding
-    // (bf16 / fp16 scales and biases are fp16-exact; SYM4's fp32 scale is
-    // not, and rounding it would bias a whole row, so SYM4 stays in fp32)
-    half2_t s2, t2;
-    s2.x = s2.y = (_Float16)S;
-    t2.x = t2.y = (_Float16)T;
-    const half2_t mag = {(_Float16)1024.f, (_Float16)1024.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t m = and_or(st.w[i][j] >> (4 * e), 0x000F000Fu, magic);
-      const half2_t q = __builtin_bit_cast(half2_t, m) - mag;
-      p[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, s2, t2));
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p[e] = pack_f16(fmaf((float)sk_field<KIND>(st.w[i], st.h[i], j, e), S, T),
-                      fmaf((float)sk_field<KIND>(st.w[i], st.h[i], j, e + 4), S, T));
-  }
-  return __builtin_bit_cast(half8_t, make_uint4(p[0], p[1], p[2], p[3]));
-}
-
-struct SkRsrc {
-  __amdgpu_buffer_rsrc_t x, w, h, s, z, p;
-  uint32_t xo;                          // activation row r, lane's columns (kOOB if r >= M)
-  uint32_t wo[2], ho[2], so[2], zo[2], po[2];
-  uint32_t g;                           // lane >> 4
-};
-
-template <int KIND, bool PERCH, bool LM>
-__device__ __forceinline__ void sk_load(const SkinnyArgs& a, const SkRsrc& r, int kb,
-                                        SkStage<KIND>& st) {
-  st.kb = kb;
-  const uint32_t c0 = (uint32_t)kb * kSkCols + 32u * r.g;   // lane's first column
-  // activations: 32 columns = 64 bytes (rows past M read 0)
-  const uint32_t xo = r.xo == 0xFFFFFFFFu ? 0x80000000u : r.xo + 2u * c0;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    st.x[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.x, xo + 16u * t, 0, 0));
-  constexpr int W = GT<KIND>::W;   // code words per 64 columns; a lane takes W / 2
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t wk = r.wo[i] + c0 * (uint32_t)(W / 2) / 8u;   // bytes: c0 * bits / 8
-    if constexpr (W == 4) {
-      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.w, wk, 0, 0));
-      st.w[i][0] = v.x; st.w[i][1] = v.y;
-    } else {
-#pragma unroll
-      for (int c = 0; c < W / 8; ++c) {
-        const uint4 v = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(r.w, wk + 16u * c, 0, 0));
-        st.w[i][4 * c] = v.x; st.w[i][4 * c + 1] = v.y;
-        st.w[i][4 * c + 2] = v.z; st.w[i][4 * c + 3] = v.w;
-      }
-    }
-    st.s0[i] = st.s1[i] = st.s2[i] = 0;
-    if constexpr (LM) {
-      if constexpr (KIND == G_Q6K) {   // the high plane is code data, not metadata
-        const uint2 v = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho[i] + c0 / 4u, 0, 0));
-        st.h[i][0] = v.x; st.h[i][1] = v.y;
-      }
-    } else if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
-      const uint32_t g = c0 / (uint32_t)a.gs;
-      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so[i] + 2u * g, 0, 0);
-      st.s1[i] = __builtin_amdgcn_raw_buffer_load_b16(r.z, r.zo[i] + 2u * g, 0, 0);
-    } else if constexpr (KIND == G_Q4K) {
-      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b8(r.s, r.so[i] + c0 / 32u, 0, 0);
-      st.s1[i] = __builtin_amdgcn_raw_buffer_load_b8(r.z, r.zo[i] + c0 / 32u, 0, 0);
-      st.s2[i] = __builtin_amdgcn_raw_buffer_load_b32(r.p, r.po[i] + 4u * (c0 / 256u), 0, 0);
-    } else if constexpr (KIND == G_Q6K) {
-      const uint2 v = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(r.h, r.ho[i] + c0 / 4u, 0, 0));
-      st.h[i][0] = v.x; st.h[i][1] = v.y;
-      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b16(r.s, r.so[i] + c0 / 16u, 0, 0);
-      st.s2[i] = __builtin_amdgcn_raw_buffer_load_b16(r.p, r.po[i] + 2u * (c0 / 256u), 0, 0);
-    } else if constexpr (!PERCH) {
-      st.s0[i] = __builtin_amdgcn_raw_buffer_load_b32(r.s, r.so[i] + 4u * (c0 / (uint32_t)a.gs), 0, 0);
-    }
-  }
-}
-
-// Metadata of a stage's column block for the lane's two rows, from the
-// block's LDS copy (the same fields sk_load reads from HBM otherwise).
-template <int KIND, bool PERCH>
-__device__ __forceinline__ void sk_meta_lds(const SkinnyArgs& a, const unsigned char* smem,
-                                            int rr, uint32_t g4, SkStage<KIND>& st) {
-  const uint32_t c0 = (uint32_t)st.kb * kSkCols + 32u * g4;
-  const uint32_t K = (uint32_t)a.K;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t n = 16u * i + (uint32_t)rr;
-    if constexpr (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) {
-      const uint32_t off = n * (K / (uint32_t)a.gs) * 2u + 2u * (c0 / (uint32_t)a.gs);
-      st.s0[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[0] + off);
-      st.s1[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[1] + off);
-    } else if constexpr (KIND == G_Q4K) {
-      st.s0[i] = smem[a.lds_meta[0] + n * (K / 32u) + c0 / 32u];
-      st.s1[i] = smem[a.lds_meta[1] + n * (K / 32u) + c0 / 32u];
-      st.s2[i] = *reinterpret_cast<const uint32_t*>(smem + a.lds_meta[2] + n * (K / 256u) * 4u +
-                                                    4u * (c0 / 256u));
-    } else if constexpr (KIND == G_Q6K) {
-      st.s0[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[0] + n * (K / 16u) + c0 / 16u);
-      st.s2[i] = *reinterpret_cast<const uint16_t*>(smem + a.lds_meta[2] + n * (K / 256u) * 2u +
-                                                    2u * (c0 / 256u));
-    } else if constexpr (!PERCH) {
-      st.s0[i] = *reinterpret_cast<const uint32_t*>(smem + a.lds_meta[0] + n * (K / (uint32_t)a.gs) * 4u +
-                                                    4u * (c0 / (uint32_t)a.gs));
-    }
-  }
-}
-
-template <int KIND, bool XBF16, bool MBF16, bool PERCH, bool LM>
-__global__ void __launch_bounds__(64 * kSkWaves) k_skinny(SkinnyArgs a) {
-  // LDS: partial sums [wave][tile][weight row][activation row] first, then
-  // (LM) the block's metadata rows
-  extern __shared__ __attribute__((aligned(16))) unsigned char sk_smem[];
-  float (*part)[2][16][17] = reinterpret_cast<float (*)[2][16][17]>(sk_smem);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rr = lane & 15;
-  const int64_t n0 = (int64_t)blockIdx.x * kSkRows;
-  const int64_t nrows = a.N - n0 < kSkRows ? a.N - n0 : kSkRows;
-  const int64_t K = a.K;
-  const int KB = (int)(K / kSkCols);
-
-  SkRsrc r;
-  {
-    r.g = (uint32_t)(lane >> 4);
-    r.x = rsrc(a.x, (uint32_t)(a.M * K * 2));
-    r.xo = rr < a.M ? (uint32_t)(rr * K * 2) : 0xFFFFFFFFu;
-    const int64_t wrow = (KIND == G_AFF2 ? K / 4 : KIND == G_AFF8 ? K : K / 2);
-    int64_t srow = 0, zrow = 0, prow = 0;
-    if constexpr (KIND == G_Q4K) { srow = K / 32; zrow = K / 32; prow = (K / 256) * 4; }
-    else if constexpr (KIND == G_Q6K) { srow = K / 16; prow = (K / 256) * 2; }
-    else if constexpr (KIND == G_SYM4) { srow = (K / a.gs) * 4; }
-    else { srow = (K / a.gs) * 2; zrow = srow; }
-    r.w = rsrc(static_cast<const unsigned char*>(a.qw) + n0 * wrow, (uint32_t)(nrows * wrow));
-    r.h = r.w;
-    if constexpr (KIND == G_Q6K)
-      r.h = rsrc(static_cast<const unsigned char*>(a.qh) + n0 * (K / 4), (uint32_t)(nrows * (K / 4)));
-    r.s = rsrc(static_cast<const unsigned char*>(a.scales) + n0 * srow, (uint32_t)(nrows * srow));
-    r.z = zrow ? rsrc(static_cast<const unsigned char*>(a.zeros) + n0 * zrow, (uint32_t)(nrows * zrow))
-               : r.s;
-    r.p = prow ? rsrc(static_cast<const unsigned char*>(a.steps) + n0 * prow, (uint32_t)(nrows * prow))
-               : r.s;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t n = 16 * i + rr;
-      r.wo[i] = (uint32_t)(n * wrow);
-      r.ho[i] = (uint32_t)(n * (K / 4));
-      r.so[i] = (uint32_t)(n * srow);
-      r.zo[i] = (uint32_t)(n * zrow);
-      r.po[i] = (uint32_t)(n * prow);
-    }
-  }
-
-  typedef float float4_t __attribute__((ext_vector_type(4)));
-  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-  float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  float4_t acc_c = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t magic = 0x64006400u;
-  // Per-channel SYM4 with bf16 activations runs on bf16 MFMA: the codes as
-  // bf16 are 128 + u exactly (0x4300 | u), the activations need only the
-  // column reorder, and one more MFMA per step with the constant -136 (the
-  // code offset 8 plus 128) accumulates -136 * sum(x) into acc_c, which is
-  // added to every tile at the end: sum (128 + u - 136) x = sum q x, exact
-  // products, fp32 accumulation.
-  constexpr bool BF = PERCH && XBF16;
-  const uint32_t magic_bf = 0x43004300u;
-  const bf16x8_t neg136 = __builtin_bit_cast(bf16x8_t, make_uint4(0xC308C308u, 0xC308C308u,
-                                                                 0xC308C308u, 0xC308C308u));
-
-  auto compute = [&](SkStage<KIND>& st) {
-    if constexpr (LM) sk_meta_lds<KIND, PERCH>(a, sk_smem, rr, r.g, st);
-    if constexpr (BF) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, act_chunk<false>(st.x[t]));   // reorder only
-        acc_c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(neg136, B, acc_c, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          uint32_t p[4];
-#pragma unroll
-          // plain C, not the inline-asm and_or: these values feed the MFMA
-          // directly, and only compiler-visible producers get the VALU-write
-          // -> MFMA-read wait states the hardware needs
-          for (int e = 0; e < 4; ++e) p[e] = ((st.w[i][t] >> (4 * e)) & 0x000F000Fu) | magic_bf;
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, make_uint4(p[0], p[1], p[2], p[3])), B, acc[i], 0, 0, 0);
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const half8_t B = __builtin_bit_cast(half8_t, act_chunk<XBF16>(st.x[t]));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sk_weight_frag<KIND, MBF16, PERCH>(st, i, t, magic),
-                                                        B, acc[i], 0, 0, 0);
-    }
-  };
-
-  // the wave's column blocks: wave, wave + kSkWaves, ...; kSkDepth blocks in
-  // flight ahead of the one being computed (a ring of kSkDepth + 1 stages,
-  // unrolled so every stage index is a compile-time constant)
-  constexpr int R = kSkDepth + 1;
-  SkStage<KIND> st[R];
-  const int J = wave < KB ? (KB - wave + kSkWaves - 1) / kSkWaves : 0;   // blocks of this wave
-  static_for<kSkDepth>([&](auto P) {
-    constexpr int p = decltype(P)::value;
-    if (p < J) sk_load<KIND, PERCH, LM>(a, r, wave + p * kSkWaves, st[p]);
-  });
-  if constexpr (LM) {
-    // copy the metadata rows [n0, n0 + 32) of every array into LDS in
-    // 16-byte units (rows are contiguous; the allocations are 16-byte
-    // multiples, so the rounded-up tail stays inside them)
-    const unsigned char* src[3] = {static_cast<const unsigned char*>(a.scales),
-                                   static_cast<const unsigned char*>(a.zeros),
-                                   static_cast<const unsigned char*>(a.steps)};
-    const uint32_t rowb[3] = {KIND == G_Q4K ? (uint32_t)(K / 32)
-                              : KIND == G_Q6K ? (uint32_t)(K / 16)
-                              : KIND == G_SYM4 ? (uint32_t)(K / a.gs) * 4u
-                                               : (uint32_t)(K / a.gs) * 2u,
-                              KIND == G_Q4K ? (uint32_t)(K / 32)
-                              : (KIND == G_AFF2 || KIND == G_AFF4 || KIND == G_AFF8) ? (uint32_t)(K / a.gs) * 2u
-                                                                                     : 0u,
-                              KIND == G_Q4K ? (uint32_t)(K / 256) * 4u
-                              : KIND == G_Q6K ? (uint32_t)(K / 256) * 2u : 0u};
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      if (rowb[q] == 0 || (PERCH && q == 0)) continue;
-      const uint64_t start = (uint64_t)n0 * rowb[q];
-      const auto rs = rsrc(src[q] + start, (uint32_t)(a.meta_bytes[q] - start));
-      const uint32_t units = ((uint32_t)nrows * rowb[q] + 15u) / 16u;
-      for (uint32_t u = (uint32_t)tid; u < units; u += 64u * kSkWaves)
-        *reinterpret_cast<uint4*>(sk_smem + a.lds_meta[q] + 16u * u) =
-            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16u * u, 0, 0));
-    }
-    __syncthreads();
-  }
-  for (int j0 = 0; j0 < J; j0 += R) {
-    static_for<R>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const int j = j0 + q;
-      if (j < J) {
-        if (j + kSkDepth < J)
-          sk_load<KIND, PERCH, LM>(a, r, wave + (j + kSkDepth) * kSkWaves, st[(q + kSkDepth) % R]);
-        compute(st[q]);
-      }
-    });
-  }
-
-  if constexpr (BF) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] += acc_c;
-  }
-  // ---- partial sums of the 8 waves meet in LDS
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) part[wave][i][4 * (lane >> 4) + v][rr] = acc[i][v];
-  __syncthreads();
-  // thread -> (weight row 0..31, activation row 0..15)
-  const int nl = tid >> 4, m = tid & 15;
-  const int64_t n = n0 + nl;
-  if (m < a.M && n < a.N) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) sum += part[w][nl >> 4][nl & 15][m];
-    if constexpr (PERCH) sum *= static_cast<const float*>(a.scales)[n];
-    if (a.bias) {
-      const uint32_t bb = static_cast<const uint16_t*>(a.bias)[n];
-      sum += XBF16 ? bf16_to_f32(bb) : f16_to_f32(bb);
-    }
-    const int64_t idx = (int64_t)m * a.N + n;
-    if (a.ydt == F32) static_cast<float*>(a.y)[idx] = sum;
-    else static_cast<uint16_t*>(a.y)[idx] =
-        (uint16_t)(a.ydt == BF16 ? f32_to_bf16_rne(sum) : f32_to_f16_rne(sum));
-  }
-}
-
 }  // namespace
-
-bool skinny_supported(const Desc& d) { return d.K % kSkCols == 0; }
-
-hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
-                         const void* bias, void* y, int ydt, const size_t bytes[5],
-                         hipStream_t s) {
-  if (M < 1 || M > 16 || !skinny_supported(d)) return hipErrorInvalidValue;
-  SkinnyArgs a;
-  a.qw = b.qweight;
-  a.qh = b.qweight_hi;
-  a.scales = b.scales;
-  a.zeros = b.zeros;
-  a.steps = b.steps;
-  a.x = x;
-  a.bias = bias;
-  a.y = y;
-  a.M = M;
-  a.N = d.N;
-  a.K = d.K;
-  a.gs = d.gs;
-  a.ydt = ydt;
-  const bool xb = xdt == BF16, mb = d.meta == BF16;
-  // metadata row bytes per array; staged in LDS when a block's rows fit
-  uint32_t rowb[3] = {0, 0, 0};
-  const uint32_t K = (uint32_t)d.K;
-  if (d.fmt == AFFINE) rowb[0] = rowb[1] = (K / d.gs) * 2u;
-  else if (d.fmt == Q4K) { rowb[0] = rowb[1] = K / 32u; rowb[2] = (K / 256u) * 4u; }
-  else if (d.fmt == Q6K) { rowb[0] = K / 16u; rowb[2] = (K / 256u) * 2u; }
-  else rowb[0] = (K / d.gs) * 4u;
-  uint32_t lds = (uint32_t)(sizeof(float) * kSkWaves * 2 * 16 * 17);
-  uint32_t metab = 0;
-  for (int q = 0; q < 3; ++q) {
-    a.meta_bytes[q] = (uint32_t)((bytes[2 + q] + 15) & ~size_t(15));
-    a.lds_meta[q] = lds + metab;
-    metab += (kSkRows * rowb[q] + 15u) & ~15u;
-  }
-  const bool lm = !(d.fmt == SYM4 && d.gs == d.K) && metab <= 64u * 1024u;
-  if (lm) lds += metab;
-  void (*fn)(SkinnyArgs) = nullptr;
-#define QP_SK(KD, MB) \
-  fn = lm ? (xb ? k_skinny<KD, true, MB, false, true> : k_skinny<KD, false, MB, false, true>) \
-          : (xb ? k_skinny<KD, true, MB, false, false> : k_skinny<KD, false, MB, false, false>);
-  if (d.fmt == AFFINE) {
-    if (d.bits == 2) { if (mb) { QP_SK(G_AFF2, true) } else { QP_SK(G_AFF2, false) } }
-    else if (d.bits == 4) { if (mb) { QP_SK(G_AFF4, true) } else { QP_SK(G_AFF4, false) } }
-    else { if (mb) { QP_SK(G_AFF8, true) } else { QP_SK(G_AFF8, false) } }
-  } else if (d.fmt == Q4K) {
-    QP_SK(G_Q4K, false)
-  } else if (d.fmt == Q6K) {
-    QP_SK(G_Q6K, false)
-  } else if (d.gs == d.K) {
-    fn = xb ? k_skinny<G_SYM4, true, false, true, false> : k_skinny<G_SYM4, false, false, true, false>;
-  } else {
-    QP_SK(G_SYM4, false)
-  }
-#undef QP_SK
-  const unsigned blocks = (unsigned)((d.N + kSkRows - 1) / kSkRows);
-  hipLaunchKernelGGL(fn, dim3(blocks), dim3(64 * kSkWaves), lds, s, a);
-  return hipGetLastError();
-}
 
 namespace {
 
@@ -1390,18 +1004,6 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
                        const void* bias, void* y, int ydt, void* ws, hipStream_t s) {
   const size_t wsb = ws ? gemm_workspace_bytes(d, M) : 0;
   const bool n224 = wsb > 0;
-  if (n224) {
-    const uint32_t nchunks = (uint32_t)(wsb / 16u);
-    const unsigned xblocks = (nchunks + 255u) / 256u;
-    if (xdt == BF16)
-      hipLaunchKernelGGL(k_xprep<true>, dim3(xblocks), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
-                         (uint32_t)d.K, nchunks);
-    else
-      hipLaunchKernelGGL(k_xprep<false>, dim3(xblocks), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
-                         (uint32_t)d.K, nchunks);
-  }
   GemmArgs a;
   a.qw = b.qweight;
   a.qh = b.qweight_hi;
@@ -1419,6 +1021,21 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.ydt = ydt;
   a.tilesM = (int)((M + BM - 1) / BM);
   a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
+  if (xdt == BF16)   // per-row prescale exponents into y (see k_xexp)
+    hipLaunchKernelGGL(k_xexp, dim3((unsigned)M), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       d.K, y, d.N, ydt, n224 ? BN7 : BN, a.tilesN);
+  if (n224) {
+    const uint32_t nchunks = (uint32_t)(wsb / 16u);
+    const unsigned xblocks = (nchunks + 255u) / 256u;
+    if (xdt == BF16)
+      hipLaunchKernelGGL(k_xprep<true>, dim3(xblocks), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
+                         (uint32_t)d.K, nchunks, a);
+    else
+      hipLaunchKernelGGL(k_xprep<false>, dim3(xblocks), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
+                         (uint32_t)d.K, nchunks, a);
+  }
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   const bool xb = xdt == BF16, mb = d.meta == BF16, g32 = d.gs == 32;
   // chunked affine metadata: whole 8-group chunks per row (16-byte aligned)

@@ -16,8 +16,9 @@
 //  * Activations.  With one activation row the block stages x in LDS next to
 //    the metadata; each lane takes its slice from there (SYM4: the block
 //    builds the pairs once), rearranged into the bf16 (fp16) pairs that
-//    match the code pairs, and reuses it for every row.  With several rows
-//    (M tile > 1) each lane loads its slices directly.
+//    match the code pairs (one v_perm_b32 per pair) with their sums (v_dot2
+//    against (1, 1)), and reuses it for every row.  With several rows (M
+//    tile > 1) each lane loads its slices directly.
 //  * Arithmetic.  Codes become bf16 (fp16) pairs without a conversion
 //    instruction: v_perm_b32 places a code byte under the high byte of 128.0
 //    bf16 (1024.0 fp16), which is exactly 128 + q (1024 + q).  One v_dot2
@@ -171,23 +172,22 @@ __device__ __forceinline__ uint32_t pair_bytes13(uint32_t codes, uint32_t magic)
 #ifndef QP_GEMV_LOADS_PER_BATCH
 #define QP_GEMV_LOADS_PER_BATCH 4   // 16-byte code loads per lane, double-buffered mode
 #endif
-#ifndef QP_GEMV_SINGLE_LOADS
-#define QP_GEMV_SINGLE_LOADS 8      // 16-byte code loads per lane, single-batch mode
-#endif
 #ifndef QP_GEMV_MIN_WAVES_PER_EU
 #define QP_GEMV_MIN_WAVES_PER_EU 2
 #endif
-#ifndef QP_GEMV_EARLY_ROWS
-#define QP_GEMV_EARLY_ROWS 3        // first-batch rows requested before the prologue wait
-#endif
 
-__host__ __device__ constexpr int single_loads(int k) {
-  const int kind = base_kind(k);
-  // formats with more registers per chunk (2-bit: 32 activation pairs;
-  // int6: a second code plane) get a smaller budget
-  return kind == K_AFF2 ? (QP_GEMV_SINGLE_LOADS > 8 ? 8 : QP_GEMV_SINGLE_LOADS)
-                        : (kind == K_Q6K ? QP_GEMV_SINGLE_LOADS * 3 / 4 : QP_GEMV_SINGLE_LOADS);
+// Single-batch mode, per format (timed on the decode layers): int4 affine
+// and Q4K request up to 14 loads per lane (7 rows of two chunks at K = 4096)
+// and all of them before the prologue wait; the other formats do best with
+// 8 loads (int6, with its second code plane, 6), three rows of which go out
+// before the wait.
+__host__ __device__ constexpr bool wide_single(int k) {
+  return base_kind(k) == K_AFF4 || base_kind(k) == K_Q4K;
 }
+__host__ __device__ constexpr int single_loads(int k) {
+  return wide_single(k) ? 14 : (base_kind(k) == K_Q6K ? 6 : 8);
+}
+__host__ __device__ constexpr int early_rows(int k) { return wide_single(k) ? 8 : 3; }
 
 // Rows per batch.  Double-buffered mode (NB = 2): enough 16-byte loads per
 // lane in flight while the other batch is computed, fewer rows when the M
@@ -236,6 +236,131 @@ __device__ __forceinline__ T lds_read(const uint8_t* smem, uint32_t byte) {
   return *reinterpret_cast<const T*>(smem + byte);
 }
 
+// Scale S and offset T of each part of one chunk (see the file comment):
+// its contribution is S * (dot of codes and activations) + T * (sum of the
+// activations).  m0..m2: LDS byte offsets of the row's staged scales,
+// biases / zero codes and steps; meta: the lane's byte offset(s) in the
+// row; step: the lane's step offset (kOOB for lanes that do not lead 8).
+template <int KIND, bool XBF16, int GP>
+__device__ __forceinline__ void chunk_meta(const uint8_t* smem, uint32_t m0, uint32_t m1,
+                                           uint32_t m2, const uint32_t (&meta)[GP],
+                                           uint32_t step, float (&S)[GP], float (&Tt)[GP]) {
+  constexpr int BK = base_kind(KIND);
+  constexpr float MAGF = XBF16 ? 128.f : 1024.f;
+  if constexpr (is_affine(KIND)) {
+#pragma unroll
+    for (int p = 0; p < GP; ++p) {
+      const uint32_t sb = lds_read<uint16_t>(smem, m0 + meta[p]);
+      const uint32_t bb = lds_read<uint16_t>(smem, m1 + meta[p]);
+      const float sv = meta_is_bf16(KIND) ? bf16_to_f32(sb) : f16_to_f32(sb);
+      const float bv = meta_is_bf16(KIND) ? bf16_to_f32(bb) : f16_to_f32(bb);
+      S[p] = sv;
+      Tt[p] = (BK == K_AFF8) ? bv : fmaf(-MAGF, sv, bv);
+    }
+  } else if constexpr (BK == K_Q4K) {
+    uint32_t st = 0;
+    if (step != kOOB) st = lds_read<uint32_t>(smem, m2 + step);
+    st = bcast8(st);
+    const float Sv = (float)lds_read<uint8_t>(smem, m0 + meta[0]) * f16_to_f32(st & 0xFFFFu);
+    const float Z = (float)lds_read<uint8_t>(smem, m1 + meta[0]) * f16_to_f32(st >> 16);
+    S[0] = Sv;
+    Tt[0] = -Sv * (MAGF + Z);
+  } else if constexpr (BK == K_Q6K) {
+    uint32_t st = 0;
+    if (step != kOOB) st = lds_read<uint16_t>(smem, m2 + step);
+    st = bcast8(st);
+    const float stp = f16_to_f32(st & 0xFFFFu);
+    const uint32_t sc2 = lds_read<uint16_t>(smem, m0 + meta[0]);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float Sv = (float)(int)(int8_t)(sc2 >> (8 * p)) * stp;
+      S[p] = Sv;
+      Tt[p] = -Sv * (MAGF + 32.f);
+    }
+  } else {  // SYM4
+    const float sv = lds_read<float>(smem, m0 + meta[0]);
+    S[0] = sv;
+    Tt[0] = -sv * (MAGF + 8.f);
+  }
+}
+
+// Dot products of one 16-byte code chunk (and for Q6K its high-plane bits)
+// with the matching activation pairs: acc[m][part] = sum (MAG + q) * x
+// (8-bit codes: sum q * x).  Codes only; no metadata.
+template <int KIND, bool XBF16, int MT, int XW, int GP>
+__device__ __forceinline__ void chunk_dots(const uint4 cw, const uint2 hw,
+                                           const uint32_t (&xq)[MT][XW], float (&acc)[MT][GP]) {
+  constexpr int BK = base_kind(KIND);
+  // high byte of 128.0 bf16 (0x4300) or 1024.0 fp16 (0x6400), replicated
+  const uint32_t magic = XBF16 ? 0x43434343u : 0x64646464u;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int p = 0; p < GP; ++p) acc[m][p] = 0.f;
+  const uint32_t wv[4] = {cw.x, cw.y, cw.z, cw.w};
+  if constexpr (BK == K_AFF8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float q = (float)((wv[i] >> (8 * t)) & 0xFFu);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][0] = fmaf(q, __uint_as_float(xq[m][4 * i + t]), acc[m][0]);
+      }
+  } else if constexpr (BK == K_AFF2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        // bytes of f = codes t, 4+t, 8+t, 12+t of the word
+        const uint32_t f = (wv[i] >> (2 * t)) & 0x03030303u;
+        const uint32_t pa = pair_bytes02(f, magic);   // pair t     = (t, 8+t)
+        const uint32_t pb = pair_bytes13(f, magic);   // pair 4 + t = (4+t, 12+t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          acc[m][i / 2] = dot2<XBF16>(pa, xq[m][8 * i + t], acc[m][i / 2]);
+          acc[m][i / 2] = dot2<XBF16>(pb, xq[m][8 * i + 4 + t], acc[m][i / 2]);
+        }
+      }
+  } else if constexpr (BK == K_Q6K) {
+    // high-plane bytes reordered [b0 b2 b1 b3] so that the two codes of
+    // each pair find their 2-bit tops in the matching 16-bit halves
+    const uint32_t h0 = __builtin_amdgcn_perm(hw.x, hw.x, 0x03010200u);
+    const uint32_t h1 = __builtin_amdgcn_perm(hw.y, hw.y, 0x03010200u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t hh = (i < 2 ? h0 : h1) >> (8 * (i % 2));
+      const uint32_t lo = wv[i] & 0x0F0F0F0Fu;
+      const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t pl[4] = {pair_bytes02(lo, magic), pair_bytes02(hi, magic),
+                              pair_bytes13(lo, magic), pair_bytes13(hi, magic)};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // top 2 bits of the pair's codes moved to bits 4-5 of each half
+        const uint32_t top =
+            (s == 0 ? (hh << 4) : s == 1 ? (hh << 2) : s == 2 ? hh : (hh >> 2)) & 0x00300030u;
+        const uint32_t pr = pl[s] | top;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][i / 2] = dot2<XBF16>(pr, xq[m][4 * i + s], acc[m][i / 2]);
+      }
+    }
+  } else {  // nibbles: AFF4, Q4K, SYM4
+    // even-position nibbles to bytes, odd-position nibbles to bytes, then
+    // v_perm pairs byte b with byte b+2 under the magic high bytes
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = wv[i] & 0x0F0F0F0Fu;          // codes 0 2 4 6
+      const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;   // codes 1 3 5 7
+      const uint32_t pr[4] = {pair_bytes02(lo, magic), pair_bytes02(hi, magic),
+                              pair_bytes13(lo, magic), pair_bytes13(hi, magic)};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[m][0] = dot2<XBF16>(pr[s], xq[m][4 * i + s], acc[m][0]);
+    }
+  }
+}
+
 template <int KIND, bool XBF16, int MT, int CPL, int RB, int XW, int GP>
 __device__ __forceinline__ void compute_batch(const GemvArgs& a, const uint8_t* smem,
                                               const Batch<KIND, RB, CPL>& B,
@@ -246,10 +371,6 @@ __device__ __forceinline__ void compute_batch(const GemvArgs& a, const uint8_t* 
                                               const uint32_t (&xq)[CPL][MT][XW],
                                               const float (&xs)[CPL][MT][GP],
                                               float (&yacc)[RB][MT]) {
-  constexpr int BK = base_kind(KIND);
-  constexpr float MAGF = XBF16 ? 128.f : 1024.f;
-  // high byte of 128.0 bf16 (0x4300) or 1024.0 fp16 (0x6400), replicated
-  const uint32_t magic = XBF16 ? 0x43434343u : 0x64646464u;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -264,115 +385,10 @@ __device__ __forceinline__ void compute_batch(const GemvArgs& a, const uint8_t* 
     const uint32_t m2 = row_base[2] + lr * a.meta_row[2];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      // ---- per-part scale S and offset T (see the file comment)
       float S[GP], Tt[GP];
-      if constexpr (is_affine(KIND)) {
-#pragma unroll
-        for (int p = 0; p < GP; ++p) {
-          const uint32_t sb = lds_read<uint16_t>(smem, m0 + lane_meta[j][p]);
-          const uint32_t bb = lds_read<uint16_t>(smem, m1 + lane_meta[j][p]);
-          const float s = meta_is_bf16(KIND) ? bf16_to_f32(sb) : f16_to_f32(sb);
-          const float b = meta_is_bf16(KIND) ? bf16_to_f32(bb) : f16_to_f32(bb);
-          S[p] = s;
-          Tt[p] = (BK == K_AFF8) ? b : fmaf(-MAGF, s, b);
-        }
-      } else if constexpr (base_kind(KIND) == K_Q4K) {
-        uint32_t st = 0;
-        if (lane_step[j] != kOOB) st = lds_read<uint32_t>(smem, m2 + lane_step[j]);
-        st = bcast8(st);
-        const float Sv = (float)lds_read<uint8_t>(smem, m0 + lane_meta[j][0]) * f16_to_f32(st & 0xFFFFu);
-        const float Z = (float)lds_read<uint8_t>(smem, m1 + lane_meta[j][0]) * f16_to_f32(st >> 16);
-        S[0] = Sv;
-        Tt[0] = -Sv * (MAGF + Z);
-      } else if constexpr (base_kind(KIND) == K_Q6K) {
-        uint32_t st = 0;
-        if (lane_step[j] != kOOB) st = lds_read<uint16_t>(smem, m2 + lane_step[j]);
-        st = bcast8(st);
-        const float step = f16_to_f32(st & 0xFFFFu);
-        const uint32_t sc2 = lds_read<uint16_t>(smem, m0 + lane_meta[j][0]);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float Sv = (float)(int)(int8_t)(sc2 >> (8 * p)) * step;
-          S[p] = Sv;
-          Tt[p] = -Sv * (MAGF + 32.f);
-        }
-      } else {  // SYM4
-        const float s = lds_read<float>(smem, m0 + lane_meta[j][0]);
-        S[0] = s;
-        Tt[0] = -s * (MAGF + 8.f);
-      }
-
-      // ---- dot products of this chunk
+      chunk_meta<KIND, XBF16, GP>(smem, m0, m1, m2, lane_meta[j], lane_step[j], S, Tt);
       float acc[MT][GP];
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int p = 0; p < GP; ++p) acc[m][p] = 0.f;
-      const uint32_t wv[4] = {B.cw[rb][j].x, B.cw[rb][j].y, B.cw[rb][j].z, B.cw[rb][j].w};
-      if constexpr (base_kind(KIND) == K_AFF8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float q = (float)((wv[i] >> (8 * t)) & 0xFFu);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-              acc[m][0] = fmaf(q, __uint_as_float(xq[j][m][4 * i + t]), acc[m][0]);
-          }
-      } else if constexpr (base_kind(KIND) == K_AFF2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            // bytes of f = codes t, 4+t, 8+t, 12+t of the word
-            const uint32_t f = (wv[i] >> (2 * t)) & 0x03030303u;
-            const uint32_t pa = pair_bytes02(f, magic);   // pair t     = (t, 8+t)
-            const uint32_t pb = pair_bytes13(f, magic);   // pair 4 + t = (4+t, 12+t)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              acc[m][i / 2] = dot2<XBF16>(pa, xq[j][m][8 * i + t], acc[m][i / 2]);
-              acc[m][i / 2] = dot2<XBF16>(pb, xq[j][m][8 * i + 4 + t], acc[m][i / 2]);
-            }
-          }
-      } else if constexpr (base_kind(KIND) == K_Q6K) {
-        // high-plane bytes reordered [b0 b2 b1 b3] so that the two codes of
-        // each pair find their 2-bit tops in the matching 16-bit halves
-        const uint32_t h0 = __builtin_amdgcn_perm(B.hw[rb][j].x, B.hw[rb][j].x, 0x03010200u);
-        const uint32_t h1 = __builtin_amdgcn_perm(B.hw[rb][j].y, B.hw[rb][j].y, 0x03010200u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t hh = (i < 2 ? h0 : h1) >> (8 * (i % 2));
-          const uint32_t lo = wv[i] & 0x0F0F0F0Fu;
-          const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;
-          const uint32_t pl[4] = {pair_bytes02(lo, magic), pair_bytes02(hi, magic),
-                                  pair_bytes13(lo, magic), pair_bytes13(hi, magic)};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            // top 2 bits of the pair's codes moved to bits 4-5 of each half
-            const uint32_t top =
-                (s == 0 ? (hh << 4) : s == 1 ? (hh << 2) : s == 2 ? hh : (hh >> 2)) & 0x00300030u;
-            const uint32_t pr = pl[s] | top;
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-              acc[m][i / 2] = dot2<XBF16>(pr, xq[j][m][4 * i + s], acc[m][i / 2]);
-          }
-        }
-      } else {  // nibbles: AFF4, Q4K, SYM4
-        // even-position nibbles to bytes, odd-position nibbles to bytes, then
-        // v_perm pairs byte b with byte b+2 under the magic high bytes
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = wv[i] & 0x0F0F0F0Fu;          // codes 0 2 4 6
-          const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;   // codes 1 3 5 7
-          const uint32_t pr[4] = {pair_bytes02(lo, magic), pair_bytes02(hi, magic),
-                                  pair_bytes13(lo, magic), pair_bytes13(hi, magic)};
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-              acc[m][0] = dot2<XBF16>(pr[s], xq[j][m][4 * i + s], acc[m][0]);
-        }
-      }
+      chunk_dots<KIND, XBF16, MT, XW, GP>(B.cw[rb][j], B.hw[rb][j], xq[j], acc);
       // masked chunks carry zero codes and zero activations: they add 0
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -400,20 +416,23 @@ __device__ __forceinline__ void x_pairs(const uint32_t (&u)[KT<base_kind(KIND)>:
       sum[0] += xval<XBF16>(bits);
     }
   } else {
+    // pair s of word w = (activation s, activation s + PW) of the word's
+    // codes: the low halves of two raw words, or their high halves, joined
+    // by one v_perm_b32 (S0 supplies the low half, S1 the high half)
     constexpr int PW = (base_kind(KIND) == K_AFF2) ? 8 : 4;   // pairs per word
-    constexpr int CW = 2 * PW;                                 // codes per word
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int sidx = 0; sidx < PW; ++sidx) {
-        // pair s = (code s, code s + PW) of the word
-        const int k0 = w * CW + sidx, k1 = k0 + PW;
-        const uint32_t lo = (u[k0 / 2] >> (16 * (k0 % 2))) & 0xFFFFu;
-        const uint32_t hi = (u[k1 / 2] >> (16 * (k1 % 2))) & 0xFFFFu;
-        q[w * PW + sidx] = lo | (hi << 16);
-        const int part = (GP == 2) ? (w / 2) : 0;
-        sum[part] += xval<XBF16>(lo) + xval<XBF16>(hi);
+        const uint32_t a = u[w * PW + sidx / 2];            // activations 2t, 2t+1
+        const uint32_t b = u[w * PW + PW / 2 + sidx / 2];   // the same PW further on
+        q[w * PW + sidx] = __builtin_amdgcn_perm(a, b, (sidx & 1) ? 0x03020706u : 0x01000504u);
       }
+    // the part sums by v_dot2 against (1, 1): products exact, fp32 sums
+    const uint32_t one2 = XBF16 ? 0x3F803F80u : 0x3C003C00u;
+    constexpr int NU = KT<base_kind(KIND)>::CC / 2;
+#pragma unroll
+    for (int t = 0; t < NU; ++t) sum[GP == 2 ? t / (NU / 2) : 0] = dot2<XBF16>(u[t], one2, sum[GP == 2 ? t / (NU / 2) : 0]);
   }
 }
 
@@ -496,7 +515,7 @@ k_gemv(GemvArgs a) {
       }
     }
   }
-  // rows of the first batch requested before the wait (QP_GEMV_EARLY_ROWS)
+  // rows of the first batch requested before the wait (early_rows)
   const __amdgpu_buffer_rsrc_t rqw = rsrc(a.qw, a.qw_bytes);
   const __amdgpu_buffer_rsrc_t rqh = rsrc(a.qh, a.qh_bytes);
   uint32_t lane_cw[CPL];
@@ -505,7 +524,7 @@ k_gemv(GemvArgs a) {
     const int c = cbase + j * 64 + lane;
     lane_cw[j] = c < C ? (uint32_t)c * 16u : kOOB;
   }
-  constexpr int EARLY = QP_GEMV_EARLY_ROWS < RB ? QP_GEMV_EARLY_ROWS : RB;
+  constexpr int EARLY = early_rows(KIND) < RB ? early_rows(KIND) : RB;
   Batch<KIND, RB, CPL> B0;
   if constexpr (EARLY > 0) {
     load_batch<KIND, RB, CPL, 0, EARLY>(a, rqw, rqh, lane_cw, B0, row0, rowEnd);
@@ -818,6 +837,7 @@ hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M, const B
   const int64_t teamsTarget = (int64_t)kNumCU * QP_GEMV_WAVES_PER_CU / KW;
   uint32_t row[kMeta];
   meta_rows(d, bias != nullptr, row);
+  auto pad16 = [](uint64_t n) { return (uint32_t)((n + 15) & ~uint64_t(15)); };
   uint32_t rowMeta = 0;
   for (int i = 0; i < kMeta; ++i) rowMeta += row[i];
   // Single-batch mode when every team's rows fit one batch with at most
@@ -868,7 +888,6 @@ hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.x_bytes = (uint32_t)(M * d.K * 2);
   // metadata is copied in 16-byte units: the buffers are readable up to
   // the next multiple of 16 bytes (part of the ABI contract)
-  auto pad16 = [](uint64_t n) { return (uint32_t)((n + 15) & ~uint64_t(15)); };
   a.meta_bytes[0] = pad16(bytes[2]);
   a.meta_bytes[1] = pad16(bytes[3]);
   a.meta_bytes[2] = pad16(bytes[4]);

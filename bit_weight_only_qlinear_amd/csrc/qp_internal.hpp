@@ -42,8 +42,8 @@ bool gemv_supported(const Desc& d);
 hipError_t launch_gemv(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        const size_t bytes[5], hipStream_t s);
-// Skinny MFMA kernel for 4 <= M <= 16 (any M in 1..16 accepted): K must be a
-// multiple of 128.
+// Exact-code MFMA qGEMV, activation rows in tiles of 16 (any M): K must be
+// a multiple of 128.
 bool skinny_supported(const Desc& d);
 hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M,
                          const Bufs& b, const void* bias, void* y, int ydt,
@@ -57,5 +57,12 @@ size_t gemm_workspace_bytes(const Desc& d, int64_t M);
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        void* ws, hipStream_t s);
+
+// Per-token symmetric int8 activations: q [M, K] int8, s [M] fp32.
+hipError_t launch_quant_act(const void* x, int xdt, int64_t M, int64_t K, void* q, float* s,
+                            hipStream_t st);
+// a8w4 forward (SYM4 per output channel, K % 128 == 0, every buffer < 2 GiB).
+hipError_t launch_a8w4(const Desc& d, const void* xq, const float* xs, int64_t M, const Bufs& b,
+                       const float* bias, void* y, int ydt, hipStream_t s);
 
 }  // namespace qp

@@ -376,6 +376,39 @@ inline unsigned blocks_for(int64_t n) {
   return (unsigned)((n + kThreads - 1) / kThreads);
 }
 
+// Per-token symmetric int8 activations (the "a8" of ExecuTorch PR #16577,
+// "Arm backend: Support a8w4 for convolution and linear"; the page leaves
+// the rule open, the one taken is per row m):
+//   s_m = fl32(max_k |x[m, k]| / 127),
+//   q[m, k] = s_m == 0 ? 0 : clamp(rint(fl32(x[m, k] / s_m)), -127, 127).
+// One block per row; every step the single IEEE operation written above.
+template <bool XBF16>
+__global__ void __launch_bounds__(kThreads)
+k_quant_act(const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q, float* __restrict__ s) {
+  __shared__ float wmax[kThreads / 64];
+  const int64_t m = blockIdx.x;
+  const uint16_t* xr = x + m * K;
+  float amax = 0.f;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+    const uint32_t b = xr[k];
+    amax = fmaxf(amax, fabsf(XBF16 ? bf16_to_f32(b) : f16_to_f32(b)));
+  }
+  amax = wave_max_all(amax);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  const float sc = div_rn(amax, 127.f);
+  if (threadIdx.x == 0) s[m] = sc;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
+    const uint32_t b = xr[k];
+    const float v = XBF16 ? bf16_to_f32(b) : f16_to_f32(b);
+    const float c = sc == 0.f ? 0.f : clampf(rintf(div_rn(v, sc)), -127.f, 127.f);
+    q[m * K + k] = (int8_t)(int)c;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const Desc& d, const float* W, void* qweight,
@@ -437,6 +470,17 @@ hipError_t launch_dequant(const Desc& d, const Bufs& b, void* out, int out_dt, h
                      static_cast<const uint32_t*>(b.qweight),
                      static_cast<const uint32_t*>(b.qweight_hi), b.scales, b.zeros, b.steps,
                      out, d.N, d.K, d.fmt, d.bits, d.gs, d.meta == BF16 ? 1 : 0, out_dt);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const void* x, int xdt, int64_t M, int64_t K, void* q, float* s,
+                            hipStream_t st) {
+  if (xdt == BF16)
+    hipLaunchKernelGGL(k_quant_act<true>, dim3((unsigned)M), dim3(kThreads), 0, st,
+                       static_cast<const uint16_t*>(x), K, static_cast<int8_t*>(q), s);
+  else
+    hipLaunchKernelGGL(k_quant_act<false>, dim3((unsigned)M), dim3(kThreads), 0, st,
+                       static_cast<const uint16_t*>(x), K, static_cast<int8_t*>(q), s);
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ def _load():
         "qlinear_forward_kernel": (I32, [D, P, I32, I64, W, P, P, I32, I32, P]),
         "qlinear_workspace_bytes": (I32, [D, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "qlinear_forward_ws": (I32, [D, P, I32, I64, W, P, P, I32, I32, P, ctypes.c_size_t, P]),
+        "qpack_quantize_activations": (I32, [P, I32, I64, I64, P, P, P]),
+        "qlinear_forward_a8w4": (I32, [D, P, P, I64, W, P, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -73,7 +75,7 @@ lib = _load()
 EXPORTED = ("qpack_abi_version", "qpack_last_error", "qpack_sizes", "qpack_quantize",
             "qpack_unpack_codes", "qpack_pack_codes", "qpack_dequantize",
             "qlinear_forward", "qlinear_forward_kernel", "qlinear_workspace_bytes",
-            "qlinear_forward_ws")
+            "qlinear_forward_ws", "qpack_quantize_activations", "qlinear_forward_a8w4")
 
 
 @dataclass(frozen=True)
@@ -252,4 +254,31 @@ def qlinear_forward(desc: QDesc, x, w, bias=None, y_dtype: Optional[str] = None,
     _check(lib.qlinear_forward_ws(ctypes.byref(d), _ptr(x), DTYPE_IDS[xd], M,
                                   ctypes.byref(ws), _ptr(bias), _ptr(out), DTYPE_IDS[yd],
                                   kernel, _ptr(buf), nbytes, _stream(x.device)))
+    return out
+
+
+def quantize_activations(x):
+    """Per-token symmetric int8 activations (qpack_quantize_activations):
+    x fp16/bf16 [M, K] -> (xq int8 [M, K], xs fp32 [M])."""
+    import torch
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(lib.qpack_quantize_activations(_ptr(x), DTYPE_IDS[_xdtype(x)], M, K, _ptr(xq),
+                                          _ptr(xs), _stream(x.device)))
+    return xq, xs
+
+
+def qlinear_forward_a8w4(desc: QDesc, xq, xs, w, bias=None, y_dtype: str = "bf16", out=None):
+    """y [M, N] = xs[m] * s_n * sum_k xq[m, k] q[n, k] (+ bias fp32 [N]) for
+    SYM4 weights with one scale per output channel."""
+    import torch
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[y_dtype]
+    M = xq.shape[0]
+    if out is None:
+        out = torch.empty((M, desc.N), dtype=tdt, device=xq.device)
+    d, ws = desc.c(), _wstruct(w)
+    _check(lib.qlinear_forward_a8w4(ctypes.byref(d), _ptr(xq), _ptr(xs), M, ctypes.byref(ws),
+                                    _ptr(bias), _ptr(out), DTYPE_IDS[y_dtype],
+                                    _stream(xq.device)))
     return out

@@ -78,8 +78,7 @@
  *     nested formats), supported (fmt, bits, group_size, dtype) combinations,
  *     alignment, N, K, M > 0.
  *   * Inputs must be finite; non-finite weights or activations give
- *     unspecified results.  Activations are used exactly when fp16 / bf16
- *     values; see qlinear_forward for the one exception.
+ *     unspecified results.
  */
 #ifndef QLINEAR_H
 #define QLINEAR_H
@@ -113,15 +112,17 @@ typedef enum { QP_F16 = 0, QP_BF16 = 1, QP_F32 = 2 } qp_dtype;
 
 /* Which kernel family qlinear_forward_kernel uses. */
 typedef enum {
-  QP_KERNEL_AUTO = 0,      /* small M: qGEMV; from M = 2 (per-channel SYM4),
+  QP_KERNEL_AUTO = 0,      /* M <= 8: qGEMV; from M = 2 (per-channel SYM4),
                               4 (Q6K) or 3 (other formats) up to M = 16: MFMA
-                              qGEMV when K % 128 == 0 and K <= 16384 (else
-                              qGEMV up to M = 8); larger M: qGEMM            */
+                              qGEMV when K % 128 == 0; larger M: qGEMM up to
+                              K = 8192, the MFMA qGEMV beyond                 */
   QP_KERNEL_GEMV = 1,      /* decode-shaped kernel, any M (processed 8 at once) */
-  QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M; K % 64 == 0,
-                              K <= 2^22                                      */
-  QP_KERNEL_GEMV_MFMA = 3  /* decode-shaped MFMA kernel, M <= 16, K % 128 == 0,
-                              every buffer < 2 GiB                           */
+  QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M; fp16-rounded
+                              weights, so K % 64 == 0 and K <= 8192, where it
+                              meets the output bound                          */
+  QP_KERNEL_GEMV_MFMA = 3  /* MFMA qGEMV on exact codes, any M (tiles of 16
+                              activation rows), K % 128 == 0, every buffer
+                              < 2 GiB                                         */
 } qp_kernel;
 
 typedef struct {
@@ -186,16 +187,18 @@ qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out,
 /* y [M, N] (y_dtype, row-major) = x [M, K] (x_dtype, row-major) * W^T
  * (+ bias [N], x_dtype, or NULL).  x_dtype: QP_F16 or QP_BF16.  y_dtype:
  * QP_F16, QP_BF16 or QP_F32.  Accumulation is fp32.
- * The decode-shaped qGEMV (QP_KERNEL_GEMV) uses the codes exactly and
- * applies each group's scale and offset in fp32.  The MFMA kernels
- * (QP_KERNEL_GEMV_MFMA for 4 <= M <= 16, QP_KERNEL_GEMM for larger M) run on
- * fp16 MFMA: each weight is dequantized and rounded once to fp16 inside the
- * kernel (scales, zero points and weights are assumed to lie in the fp16
- * normal range; the MFMA qGEMV feeds per-channel SYM4 codes exactly and
- * applies the fp32 channel scale to the result), and activations are
- * converted to fp16 (exact for bf16
- * values of magnitude in [2^-17, 65504]; larger magnitudes are unsupported
- * in those paths).  QP_KERNEL_AUTO picks by M as listed under qp_kernel. */
+ * The qGEMV (QP_KERNEL_GEMV) and the MFMA qGEMV (QP_KERNEL_GEMV_MFMA) use
+ * the codes exactly, in products with the activations in their own type,
+ * and apply each group's scale and offset in fp32.  The qGEMM
+ * (QP_KERNEL_GEMM) runs on fp16 MFMA: each weight is dequantized and
+ * rounded once to fp16 inside the kernel (scales, zero points and weights
+ * are assumed to lie in the fp16 normal range), and each activation row is
+ * scaled by a power of two that brings its largest magnitude into fp16
+ * range before it is converted (undone in fp32 after the sums), so every
+ * finite bf16 activation is taken.  To hold the per-row exponents without a
+ * workspace the qGEMM writes them into y before it computes; y's contents
+ * are undefined until the call completes.  QP_KERNEL_AUTO picks by M and K as
+ * listed under qp_kernel. */
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype,
                           int64_t M, const qp_weights* w, const void* bias,
                           void* y, int32_t y_dtype, void* stream);
@@ -233,6 +236,33 @@ qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype,
                              void* y, int32_t y_dtype, int32_t kernel,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* a8w4: int8 activations x symmetric int4 weights (ExecuTorch PR #16577,
+ * "Arm backend: Support a8w4 for convolution and linear": int4 weights in
+ * an int8 container with qmin = -7, qmax = 7, and 8-bit activations).
+ *
+ * qpack_quantize_activations: per-token symmetric int8 (the page does not
+ * fix the activation rule; this one is per row m):
+ *   xs[m] = fl32(max_k |x[m, k]| / 127),
+ *   xq[m, k] = xs[m] == 0 ? 0 : clamp(rint(fl32(x[m, k] / xs[m])), -127, 127),
+ * each step one IEEE fp32 operation, ties to even.  x: [M, K] x_dtype
+ * (QP_F16 / QP_BF16); xq: int8 [M, K]; xs: fp32 [M]; device pointers,
+ * 16-byte aligned, caller-owned. */
+qp_status qpack_quantize_activations(const void* x, int32_t x_dtype, int64_t M,
+                                     int64_t K, void* xq, float* xs, void* stream);
+
+/* qlinear_forward_a8w4: y [M, N] = xs[m] * s_n * sum_k xq[m, k] * q[n, k]
+ * (+ bias [N], fp32, or NULL), for weights in the SYM4 format with one fp32
+ * scale s_n per output channel (group_size = K; q = u - 8 from the stored
+ * nibbles).  The integer sums are exact (int8 matrix cores, int32 per K
+ * split, int64 across splits); the scaling is done in fp64 in the order
+ * ((sum * xs[m]) * s_n) + bias and rounded once to fp32, then to y_dtype
+ * (QP_F16, QP_BF16, QP_F32) to nearest-even.  Needs K % 128 == 0 and xq and
+ * the codes each below 2 GiB; other SYM4 group sizes and formats are
+ * QP_EUNSUPPORTED. */
+qp_status qlinear_forward_a8w4(const qp_desc* d, const void* xq, const float* xs,
+                               int64_t M, const qp_weights* w, const float* bias,
+                               void* y, int32_t y_dtype, void* stream);
 
 #ifdef __cplusplus
 }

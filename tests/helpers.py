@@ -102,11 +102,3 @@ def check_linear(y_dev, y_ref, x64, wmax, K, ydt, rel=2e-3, extra=None):
     assert worst <= 1.0, f"max-abs error is {worst:.3f}x the bound"
     return r, worst
 
-
-def f16_weight_bound(x64, w64):
-    """Worst-case effect of rounding every dequantized weight once to fp16
-    (relative error <= 2^-11 each): 2^-11 * sum_k |w[n,k]| |x[m,k]|, per
-    output [M, N].  The fp16-MFMA kernels may add this to the layer's
-    element bound at large K, where it outgrows it (it grows like sqrt(K)
-    against the bound)."""
-    return 2.0 ** -11 * (np.abs(x64) @ np.abs(w64).T)

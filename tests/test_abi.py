@@ -112,16 +112,15 @@ def test_forward_argument_validation(q):
     assert _call_forward(q, q.QDesc.q4k(64, 512), w=w) == q.QP_EINVAL and "steps" in _err(q)
     w = q._Weights(FAKE, None, FAKE, None, FAKE)
     assert _call_forward(q, q.QDesc.q6k(64, 512), w=w) == q.QP_EINVAL and "qweight_hi" in _err(q)
-    # the MFMA kernel needs K % 64 == 0 and K <= 2^22
+    # the qGEMM (fp16-rounded weights) needs K % 64 == 0 and K <= 8192, where
+    # it meets the output bound
     assert _call_forward(q, q.QDesc.affine(8, 96, 4, 32), kernel=2) == q.QP_EUNSUPPORTED
-    assert _call_forward(q, q.QDesc.affine(8, 1 << 23, 4, 64), M=64,
-                         kernel=2) == q.QP_EUNSUPPORTED and "2^22" in _err(q)
-    # the MFMA qGEMV needs K % 128 == 0 and M <= 16
+    assert _call_forward(q, q.QDesc.affine(8, 16384, 4, 64), M=64,
+                         kernel=2) == q.QP_EUNSUPPORTED and "8192" in _err(q)
+    # the MFMA qGEMV needs K % 128 == 0 (any M: tiles of 16 activation rows)
     assert _call_forward(q, q.QDesc.affine(8, 192, 4, 64), M=4,
                          kernel=q.QP_KERNEL_GEMV_MFMA) == q.QP_EUNSUPPORTED
     assert "K % 128" in _err(q)
-    assert _call_forward(q, q.QDesc.affine(8, 256, 4, 64), M=17,
-                         kernel=q.QP_KERNEL_GEMV_MFMA) == q.QP_EUNSUPPORTED
 
 
 def test_other_entry_points_validate(q):
@@ -161,8 +160,8 @@ def test_workspace_query_and_checks(q):
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 0, 2, ctypes.byref(n)) == q.QP_ESHAPE
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 64, 2, None) == q.QP_EINVAL
     # past 2^31 staged bytes the qGEMM runs without a workspace
-    big = q.QDesc.affine(64, 1 << 16).c()
-    assert q.lib.qlinear_workspace_bytes(ctypes.byref(big), 1, 1 << 15, 2,
+    big = q.QDesc.affine(64, 8192).c()
+    assert q.lib.qlinear_workspace_bytes(ctypes.byref(big), 1, 1 << 18, 2,
                                          ctypes.byref(n)) == q.QP_OK
     assert n.value == 0
     w = q._Weights(FAKE, None, FAKE, FAKE, None)

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 from bit_weight_only_qlinear_amd import synth
-from helpers import (f16_weight_bound, qformat_of, to_dev_bits, oracle_buffers, gpu_rows, check_linear,
+from helpers import (qformat_of, to_dev_bits, oracle_buffers, gpu_rows, check_linear,
                      buf_to_np, y_to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -120,11 +120,10 @@ def test_quantize_exhaustive_codes_roundtrip(q):
 
 
 # --------------------------------------------------------------- forward
-def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_weights=False,
-                  workspace="auto"):
+def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, workspace="auto", xbits=None):
     W = _weights(d.N, d.K, seed)
     rng = np.random.default_rng(seed + 1)
-    xb = synth.draw_activations(rng, M, d.K, xdtype)
+    xb = synth.draw_activations(rng, M, d.K, xdtype) if xbits is None else xbits
     x64 = oracle.decode_activations(xb, xdtype)
     f = qformat_of(d)
     buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
@@ -137,8 +136,7 @@ def _forward_case(q, d, M, xdtype, ydt, kernel, seed, with_bias, rows=None, f16_
     w64 = oracle.dequant_f64(qz, f)
     b64 = oracle.decode_activations(bias_bits, xdtype) if with_bias else None
     y_ref = oracle.linear_f64(x64, qz, f, b64, w64=w64)
-    extra = f16_weight_bound(x64, w64) if f16_weights else None
-    return check_linear(y, y_ref, x64, np.abs(w64).max(), d.K, ydt, extra=extra)
+    return check_linear(y, y_ref, x64, np.abs(w64).max(), d.K, ydt)
 
 
 GEMV_SHAPES = [(1, 256), (3, 512), (77, 1024), (300, 4096), (513, 5120), (64, 8192)]
@@ -155,9 +153,10 @@ def test_gemv_forward(q, N, K, M):
 
 
 @pytest.mark.parametrize("N,K", [(1, 256), (31, 384), (77, 1024), (300, 4096), (513, 5120)])
-@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 11, 16, 17, 40])
 def test_gemv_mfma_forward(q, N, K, M):
-    """The skinny MFMA decode kernel on every format, ragged N, M up to 16."""
+    """The exact-code MFMA qGEMV on every format, ragged N, M up to 16 per
+    activation tile and several tiles."""
     for i, d in enumerate(_descs(q, N, K)):
         if K % 256 and d.fmt in ("q4k", "q6k"):
             continue
@@ -167,23 +166,63 @@ def test_gemv_mfma_forward(q, N, K, M):
                           with_bias=(i % 2 == 1))
 
 
-@pytest.mark.parametrize("fmt", ["affine32", "q4k", "q6k", "sym4g32"])
-def test_gemv_mfma_large_k(q, fmt):
-    """K = 32768: a block's metadata no longer fits LDS, so the MFMA qGEMV
-    reads it per step from HBM (the other code path of the kernel).  At this
-    K the fp16 rounding of the weights can exceed the layer's element bound,
-    so the MFMA kernels are held to it plus the fp16-weight bound.  The
-    exact-code qGEMV's register plan stops short of this K, so AUTO picks an
-    fp16-weight kernel here as well."""
+@pytest.mark.parametrize("fmt", ["affine32", "affine64", "affine2", "affine8", "q4k", "q6k",
+                                 "sym4", "sym4g32"])
+def test_large_k_exact(q, fmt):
+    """K = 32768, past the K where fp16-rounded weights hold the output
+    bound: the exact-code MFMA qGEMV (chosen by AUTO from M = 9 on, and in
+    activation tiles of 16 past M = 16) meets the plain bound; the
+    fp16-weight qGEMM refuses the shape."""
     N, K = 40, 32768
-    d = {"affine32": q.QDesc.affine(N, K, 4, 32, "bf16"), "q4k": q.QDesc.q4k(N, K),
-         "q6k": q.QDesc.q6k(N, K), "sym4g32": q.QDesc.sym4(N, K, 32)}[fmt]
-    for M in (4, 9):
-        print("gemv_mfma large K", _id(d), M, flush=True)
-        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMV_MFMA, seed=M + 7, with_bias=True,
-                      f16_weights=True)
-        _forward_case(q, d, M, "bf16", "bf16", q.QP_KERNEL_AUTO, seed=M + 8, with_bias=False,
-                      f16_weights=True)
+    d = {"affine32": q.QDesc.affine(N, K, 4, 32, "bf16"), "affine64": q.QDesc.affine(N, K, 4, 64),
+         "affine2": q.QDesc.affine(N, K, 2, 128, "f16"), "affine8": q.QDesc.affine(N, K, 8, 64),
+         "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K),
+         "sym4g32": q.QDesc.sym4(N, K, 32)}[fmt]
+    for M in (4, 16, 40):
+        print("large K", _id(d), M, flush=True)
+        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMV_MFMA, seed=M + 7, with_bias=True)
+        _forward_case(q, d, M, "bf16", "bf16", q.QP_KERNEL_AUTO, seed=M + 8, with_bias=False)
+    with pytest.raises(q.QLinearError) as e:
+        _forward_case(q, d, 40, "bf16", "f32", q.QP_KERNEL_GEMM, seed=1, with_bias=False)
+    assert e.value.status == q.QP_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt", ["affine64", "q4k", "q6k", "sym4", "sym4g32"])
+def test_gemm_max_k(q, fmt):
+    """K = 8192, the longest rows the fp16-weight qGEMM takes: the plain
+    output bound, both tilings."""
+    N, K, M = 300, 8192, 40
+    d = {"affine64": q.QDesc.affine(N, K, 4, 64, "bf16"), "q4k": q.QDesc.q4k(N, K),
+         "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K), "sym4g32": q.QDesc.sym4(N, K, 32)}[fmt]
+    for ws in ("auto", None):
+        print("gemm max K", _id(d), M, ws, flush=True)
+        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMM, seed=3, with_bias=True, workspace=ws)
+
+
+def test_mfma_activation_range(q):
+    """bf16 activations keep their full range on both MFMA paths: rows with
+    magnitudes up to 2^20 and down to 2^-30 (beyond fp16's range both ways)
+    against the oracle, on the MFMA qGEMV and on the qGEMM (whose per-row
+    power-of-two prescale brings each row into fp16 range)."""
+    N, K = 64, 1024
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(40, K))
+    x[0] *= 2.0 ** 20
+    x[1] *= 2.0 ** -30
+    x[2, ::2] *= 2.0 ** 18          # mixed magnitudes within a row
+    x[3, 1::3] *= 2.0 ** -25
+    x[4] *= 70000.0 / np.abs(x[4]).max()
+    x[7] = 0.0                      # an all-zero row
+    x[20] *= 2.0 ** 100
+    x[33] *= 2.0 ** -100
+    bits = oracle.f32_to_bf16_bits(x.astype(np.float32))
+    for d in (q.QDesc.affine(N, K, 4, 64, "bf16"), q.QDesc.q4k(N, K), q.QDesc.q6k(N, K),
+              q.QDesc.sym4(N, K), q.QDesc.affine(N, K, 8, 32, "f16")):
+        for M in (6, 40):
+            for kernel in (q.QP_KERNEL_GEMV_MFMA, q.QP_KERNEL_GEMM, q.QP_KERNEL_AUTO):
+                print("activation range", _id(d), M, kernel, flush=True)
+                _forward_case(q, d, M, "bf16", "f32", kernel, seed=9, with_bias=False,
+                              xbits=bits[:M])
 
 
 @pytest.mark.parametrize("gs", [32, 128])
@@ -195,22 +234,6 @@ def test_gemm_sym4_group_sizes(q, gs, N, K, M):
         print("gemm sym4", _id(d), M, ws, flush=True)
         _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMM, seed=gs + M, with_bias=True,
                       workspace=ws)
-
-
-@pytest.mark.parametrize("fmt", ["affine64", "affine32", "affine128", "q4k", "q6k", "sym4",
-                                 "sym4g32", "sym4g128"])
-def test_gemm_large_k(q, fmt):
-    """K = 32768 (512 steps): the qGEMM's metadata chunk rings and staged
-    activation offsets cycle many times; both tilings, fp16-weight bound."""
-    N, K, M = 300, 32768, 40
-    d = {"affine64": q.QDesc.affine(N, K, 4, 64, "bf16"), "affine32": q.QDesc.affine(N, K, 4, 32),
-         "affine128": q.QDesc.affine(N, K, 8, 128, "f16"),
-         "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K), "sym4": q.QDesc.sym4(N, K),
-         "sym4g32": q.QDesc.sym4(N, K, 32), "sym4g128": q.QDesc.sym4(N, K, 128)}[fmt]
-    for ws in ("auto", None):
-        print("gemm large K", _id(d), M, ws, flush=True)
-        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMM, seed=3, with_bias=True,
-                      f16_weights=True, workspace=ws)
 
 
 @pytest.mark.parametrize("N,K", [(1, 256), (130, 512), (257, 1280), (64, 4096), (520, 768),
