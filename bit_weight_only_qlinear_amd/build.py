@@ -25,6 +25,10 @@ SOURCES = {
     "quant.hip": ["-ffp-contract=off"],
     "gemv.hip": [],
     "gemm.hip": [],
+    "gemm_aff2.hip": [],
+    "gemm_aff4.hip": [],
+    "gemm_aff8.hip": [],
+    "gemm_kq.hip": [],
     "skinny.hip": [],
     "a8w4.hip": [],
 }

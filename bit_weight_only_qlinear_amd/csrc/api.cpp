@@ -165,8 +165,13 @@ qp_status hip_status(hipError_t e, const char* what) {
 // bound 1e-2 * ||x|| * max|w| / sqrt(K); the kernel is held to the bound up
 // to K = 8192 (the largest K of the workloads it is verified on), and longer
 // rows take the exact-code MFMA kernel instead.
+// fp16-rounded weights hold the output bound up to K = 8192; per-channel
+// SYM4 runs on exact codes (K up to 2^20: 32-bit tile offsets)
 constexpr int64_t kGemmMaxK = 8192;
-bool gemm_ok(const qp::Desc& d) { return d.K % 64 == 0 && d.K <= kGemmMaxK; }
+bool gemm_ok(const qp::Desc& d) {
+  const bool exact = d.fmt == qp::SYM4 && d.gs == d.K;
+  return d.K % 64 == 0 && d.K <= (exact ? (int64_t(1) << 20) : kGemmMaxK);
+}
 
 }  // namespace
 
@@ -261,8 +266,8 @@ qp_status plan_forward(const qp_desc* d, qp::Desc* dd, int32_t x_dtype, int64_t 
   if (kernel == QP_KERNEL_GEMM && !gemm_ok(*dd))
     return fail(QP_EUNSUPPORTED,
                 "the qGEMM kernel (fp16-rounded weights) needs K %% 64 == 0 and K <= %lld, "
-                "where it meets the output bound (K=%lld); QP_KERNEL_AUTO and "
-                "QP_KERNEL_GEMV_MFMA use exact codes at any K",
+                "where it meets the output bound (K=%lld; per-channel SYM4: exact codes, "
+                "K <= 2^20); QP_KERNEL_AUTO and QP_KERNEL_GEMV_MFMA use exact codes at any K",
                 (long long)kGemmMaxK, (long long)dd->K);
   sizes_of(*dd, nbytes);
   bool small_bufs = (size_t)M * (size_t)dd->K * 2 < (size_t(1) << 31);

@@ -115,11 +115,13 @@ typedef enum {
   QP_KERNEL_AUTO = 0,      /* M <= 8: qGEMV; from M = 2 (per-channel SYM4),
                               4 (Q6K) or 3 (other formats) up to M = 16: MFMA
                               qGEMV when K % 128 == 0; larger M: qGEMM up to
-                              K = 8192, the MFMA qGEMV beyond                 */
+                              K = 8192 (per-channel SYM4: 2^20), the MFMA
+                              qGEMV beyond                                    */
   QP_KERNEL_GEMV = 1,      /* decode-shaped kernel, any M (processed 8 at once) */
   QP_KERNEL_GEMM = 2,      /* prefill-shaped MFMA kernel, any M; fp16-rounded
                               weights, so K % 64 == 0 and K <= 8192, where it
-                              meets the output bound                          */
+                              meets the output bound; per-channel SYM4 runs
+                              on exact codes, K <= 2^20                       */
   QP_KERNEL_GEMV_MFMA = 3  /* MFMA qGEMV on exact codes, any M (tiles of 16
                               activation rows), K % 128 == 0, every buffer
                               < 2 GiB                                         */
@@ -192,7 +194,9 @@ qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out,
  * and apply each group's scale and offset in fp32.  The qGEMM
  * (QP_KERNEL_GEMM) runs on fp16 MFMA: each weight is dequantized and
  * rounded once to fp16 inside the kernel (scales, zero points and weights
- * are assumed to lie in the fp16 normal range), and each activation row is
+ * are assumed to lie in the fp16 normal range) -- except per-channel SYM4,
+ * whose codes q are fp16-exact and whose channel scale multiplies the fp32
+ * sum -- and each activation row is
  * scaled by a power of two that brings its largest magnitude into fp16
  * range before it is converted (undone in fp32 after the sums), so every
  * finite bf16 activation is taken.  To hold the per-row exponents without a

@@ -170,9 +170,9 @@ def test_gemv_mfma_forward(q, N, K, M):
                                  "sym4", "sym4g32"])
 def test_large_k_exact(q, fmt):
     """K = 32768, past the K where fp16-rounded weights hold the output
-    bound: the exact-code MFMA qGEMV (chosen by AUTO from M = 9 on, and in
-    activation tiles of 16 past M = 16) meets the plain bound; the
-    fp16-weight qGEMM refuses the shape."""
+    bound: the exact-code MFMA qGEMV (in activation tiles of 16 past
+    M = 16) meets the plain bound; the fp16-weight qGEMM refuses the shape,
+    except for per-channel SYM4, which it runs on exact codes."""
     N, K = 40, 32768
     d = {"affine32": q.QDesc.affine(N, K, 4, 32, "bf16"), "affine64": q.QDesc.affine(N, K, 4, 64),
          "affine2": q.QDesc.affine(N, K, 2, 128, "f16"), "affine8": q.QDesc.affine(N, K, 8, 64),
@@ -182,6 +182,11 @@ def test_large_k_exact(q, fmt):
         print("large K", _id(d), M, flush=True)
         _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMV_MFMA, seed=M + 7, with_bias=True)
         _forward_case(q, d, M, "bf16", "bf16", q.QP_KERNEL_AUTO, seed=M + 8, with_bias=False)
+    if fmt == "sym4":
+        for ws in ("auto", None):
+            _forward_case(q, d, 40, "bf16", "f32", q.QP_KERNEL_GEMM, seed=1, with_bias=True,
+                          workspace=ws)
+        return
     with pytest.raises(q.QLinearError) as e:
         _forward_case(q, d, 40, "bf16", "f32", q.QP_KERNEL_GEMM, seed=1, with_bias=False)
     assert e.value.status == q.QP_EUNSUPPORTED
