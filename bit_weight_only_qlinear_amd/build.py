@@ -31,6 +31,7 @@ SOURCES = {
     "gemm_kq.hip": [],
     "skinny.hip": [],
     "a8w4.hip": [],
+    "noalloc.hip": [],
 }
 
 

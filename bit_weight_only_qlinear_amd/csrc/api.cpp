@@ -368,6 +368,31 @@ qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype, i
   return hip_status(e, what);
 }
 
+qp_status qlinear_forward_static(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
+                                 const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
+                                 int32_t kernel, void* stream) {
+  qp::Desc dd;
+  Use use;
+  size_t nbytes[5];
+  qp_status st = plan_forward(d, &dd, x_dtype, M, kernel, &use, nbytes);
+  if (st != QP_OK) return st;
+  void* ws = nullptr;
+  size_t wsb = 0;
+  if (use == USE_GEMM && qp::gemm_workspace_bytes(dd, M) > 0) {
+    wsb = qp::gemm_workspace_bytes(dd, M);
+    if (wsb > qp::static_scratch_bytes())
+      return fail(QP_EUNSUPPORTED,
+                  "qlinear_forward_static: this call stages %zu bytes of activations, more than "
+                  "the library's static scratch (%zu bytes, ceil(M / 16) * 16 * K <= %zu); use "
+                  "qlinear_forward_ws with a workspace",
+                  wsb, qp::static_scratch_bytes(), qp::static_scratch_bytes() / 2);
+    (void)hipGetLastError();
+    const hipError_t e = qp::static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+  }
+  return qlinear_forward_ws(d, x, x_dtype, M, w, bias, y, y_dtype, kernel, ws, wsb, stream);
+}
+
 qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
                                  const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
                                  int32_t kernel, void* stream) {

@@ -65,4 +65,9 @@ hipError_t launch_quant_act(const void* x, int xdt, int64_t M, int64_t K, void* 
 hipError_t launch_a8w4(const Desc& d, const void* xq, const float* xs, int64_t M, const Bufs& b,
                        const float* bias, void* y, int ydt, hipStream_t s);
 
+// Static device scratch of the allocation-free forward (noalloc.hip): its
+// size, and its address on the current device (looked up once per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
+
 }  // namespace qp

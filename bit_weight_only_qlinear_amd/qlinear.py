@@ -61,6 +61,7 @@ def _load():
         "qlinear_forward_kernel": (I32, [D, P, I32, I64, W, P, P, I32, I32, P]),
         "qlinear_workspace_bytes": (I32, [D, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "qlinear_forward_ws": (I32, [D, P, I32, I64, W, P, P, I32, I32, P, ctypes.c_size_t, P]),
+        "qlinear_forward_static": (I32, [D, P, I32, I64, W, P, P, I32, I32, P]),
         "qpack_quantize_activations": (I32, [P, I32, I64, I64, P, P, P]),
         "qlinear_forward_a8w4": (I32, [D, P, P, I64, W, P, P, I32, P]),
     }
@@ -75,7 +76,8 @@ lib = _load()
 EXPORTED = ("qpack_abi_version", "qpack_last_error", "qpack_sizes", "qpack_quantize",
             "qpack_unpack_codes", "qpack_pack_codes", "qpack_dequantize",
             "qlinear_forward", "qlinear_forward_kernel", "qlinear_workspace_bytes",
-            "qlinear_forward_ws", "qpack_quantize_activations", "qlinear_forward_a8w4")
+            "qlinear_forward_ws", "qlinear_forward_static", "qpack_quantize_activations",
+            "qlinear_forward_a8w4")
 
 
 @dataclass(frozen=True)
@@ -254,6 +256,19 @@ def qlinear_forward(desc: QDesc, x, w, bias=None, y_dtype: Optional[str] = None,
     _check(lib.qlinear_forward_ws(ctypes.byref(d), _ptr(x), DTYPE_IDS[xd], M,
                                   ctypes.byref(ws), _ptr(bias), _ptr(out), DTYPE_IDS[yd],
                                   kernel, _ptr(buf), nbytes, _stream(x.device)))
+    return out
+
+
+def qlinear_forward_static(desc: QDesc, x, w, out, bias=None, kernel: int = QP_KERNEL_AUTO):
+    """qlinear_forward_static: the forward into the caller's `out` (its dtype
+    is the output dtype) with the library's static scratch in place of a
+    workspace; the C call allocates nothing."""
+    import torch
+    yd = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[out.dtype]
+    d, ws = desc.c(), _wstruct(w)
+    _check(lib.qlinear_forward_static(ctypes.byref(d), _ptr(x), DTYPE_IDS[_xdtype(x)], x.shape[0],
+                                      ctypes.byref(ws), _ptr(bias), _ptr(out), DTYPE_IDS[yd],
+                                      kernel, _stream(x.device)))
     return out
 
 

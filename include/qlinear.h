@@ -241,6 +241,25 @@ qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc):
+ * qlinear_forward_ws without a workspace argument.  Where the call would use
+ * a workspace (see qlinear_workspace_bytes) it uses the library's static
+ * device scratch instead: 32 MiB per GPU, held from the library's load until
+ * the process ends, so ceil(M / 16) * 16 * K <= 16 Mi (e.g. M = 2048 at
+ * K = 8192); a larger staging need is QP_EUNSUPPORTED and nothing is
+ * enqueued.  Allocates nothing (no hipMalloc, no allocating library call);
+ * the scratch's device address is looked up once per device on the first
+ * call, with that device current.  Every call on a GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (other streams, other threads)
+ * race, so serialize them.  The staging kernel writes every byte the qGEMM
+ * reads, so stale contents from an earlier call are never used.  Other
+ * arguments, numerics and errors as qlinear_forward_ws. */
+qp_status qlinear_forward_static(const qp_desc* d, const void* x, int32_t x_dtype,
+                                 int64_t M, const qp_weights* w, const void* bias,
+                                 void* y, int32_t y_dtype, int32_t kernel,
+                                 void* stream);
+
 /* a8w4: int8 activations x symmetric int4 weights (ExecuTorch PR #16577,
  * "Arm backend: Support a8w4 for convolution and linear": int4 weights in
  * an int8 container with qmin = -7, qmax = 7, and 8-bit activations).
