@@ -94,7 +94,7 @@ def time_graph(fn_list, steps, warmup, warmup_s=0.0):
 # rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's reading, and
 # the hash of the kernel sources the counters were taken on.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_gemv_int4_affine_m1_k4096_n14336.md")
-KERNEL_SOURCES = ("gemv.hip", "device_common.hpp", "qp_internal.hpp")
+KERNEL_SOURCES = ("gemv.hip", "device_common.hpp")
 
 
 def kernel_source_hash():
@@ -150,6 +150,32 @@ def gemv_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
     del ws, ys
     torch.cuda.empty_cache()
     return res
+
+
+def a8w4_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
+    """The a8w4 layer: per-token int8 quantization of x, then the int8 MFMA
+    forward, per layer (both kernels timed)."""
+    import numpy as np
+    import torch
+    xd = torch.from_numpy(np.ascontiguousarray(x_bits[:M]).view(np.int16)).view(torch.bfloat16).cuda()
+    ws = make_layer_weights(q, desc, W_np, layers)
+    ys = [torch.empty((M, desc.N), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    xq = torch.empty((M, desc.K), dtype=torch.int8, device="cuda")
+    xs = torch.empty((M,), dtype=torch.float32, device="cuda")
+
+    def call(w, y):
+        q._check(q.lib.qpack_quantize_activations(q._ptr(xd), q.DTYPE_IDS["bf16"], M, desc.K,
+                                                  q._ptr(xq), q._ptr(xs), q._stream(xd.device)))
+        q.qlinear_forward_a8w4(desc, xq, xs, w, y_dtype="bf16", out=y)
+
+    fns = [(lambda w=w, y=y: call(w, y)) for w, y in zip(ws, ys)]
+    wall, ev_ms = time_graph(fns, steps, warmup)
+    s = q.qpack_sizes(desc)
+    nb = s["qweight"] + s["scales"] + M * desc.K * 2 + M * desc.N * 2
+    per = ev_ms * 1e-3 / (steps * layers)
+    del ws, ys
+    torch.cuda.empty_cache()
+    return dict(bytes_per_call=nb, us_per_call=per * 1e6, gbs=nb / per / 1e9)
 
 
 def gemm_case(q, desc, W_np, x_bits, steps, warmup, warmup_s=0.3):
@@ -353,14 +379,23 @@ def main():
                                    frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
                                    us_per_call=round(r["us_per_call"], 3)))
                 log(extras[-1])
-        del w4
+        w4s = synth.make("decode_8k", seed=0, M=16)
+        for M in (1, 4, 8, 16):
+            r = a8w4_case(q, q.QDesc.sym4(8192, 8192), w4s.W, M, w4s.x_bits, 31,
+                          max(20, args.steps // 4), args.warmup)
+            extras.append(dict(workload=f"decode a8w4 (int8 per-token activations x sym int4 "
+                                        f"per-channel) M={M} K=8192 N=8192, quantize + forward",
+                               gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                               us_per_call=round(r["us_per_call"], 3)))
+            log(extras[-1])
+        del w4, w4s
         log("generating prefill_affine weights")
         w5 = synth.make("prefill_affine", seed=0)
         r = gemm_case(q, q.QDesc.affine(14336, 4096, 4, 64, "bf16"), w5.W, w5.x_bits,
                       max(10, args.steps // 10), max(3, args.warmup // 4))
         qgemm = dict(workload="prefill qGEMM int4 affine gs64 M=2048 K=4096 N=14336, "
-                              "fp16 MFMA, fp32 accumulate, bf16 out; activation staging "
-                              "kernel + 224-row-tile kernel, both timed",
+                              "fp16 MFMA, fp32 accumulate, bf16 out; row-exponent, "
+                              "activation staging and 224-row-tile kernels, all timed",
                      value=round(r["tflops"], 2), unit="TFLOP/s",
                      peak=MFMA_F16_PEAK_TFLOPS, frac=round(r["frac"], 4),
                      us_per_call=round(r["us_per_call"], 2),

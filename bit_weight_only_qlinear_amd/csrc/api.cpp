@@ -229,6 +229,77 @@ qp_status qpack_pack_codes(const qp_desc* d, const void* codes, const qp_weights
       "qpack_pack_codes launch");
 }
 
+qp_status qpack_encode_nested(const qp_desc* d, const float* s, const float* z,
+                              const qp_weights* out, int32_t* bad, void* stream) {
+  qp::Desc dd;
+  qp_status st = check_desc(d, &dd);
+  if (st != QP_OK) return st;
+  if (dd.fmt != qp::Q4K && dd.fmt != qp::Q6K)
+    return fail(QP_EUNSUPPORTED, "qpack_encode_nested takes the Q4K or Q6K format (got %d)", dd.fmt);
+  if (!out) return fail(QP_EINVAL, "out is NULL");
+  if (!s) return fail(QP_EINVAL, "s is NULL");
+  if (dd.fmt == qp::Q4K && !z) return fail(QP_EINVAL, "Q4K needs the zero points z");
+  if (dd.fmt == qp::Q6K && z) return fail(QP_EINVAL, "Q6K has no zero points: z must be NULL");
+  if (!aligned16(s) || (z && !aligned16(z)) || (bad && !aligned16(bad)))
+    return fail(QP_EALIGN, "s, z and bad must be 16-byte aligned");
+  const void* need[3] = {out->scales, dd.fmt == qp::Q4K ? out->zeros : out->scales, out->steps};
+  for (int i = 0; i < 3; ++i) {
+    if (!need[i]) return fail(QP_EINVAL, "out->scales, out->zeros (Q4K) and out->steps must be set");
+    if (!aligned16(need[i])) return fail(QP_EALIGN, "metadata buffers must be 16-byte aligned");
+  }
+  (void)hipGetLastError();
+  return hip_status(qp::launch_encode_nested(dd, s, z, out->scales, out->zeros, out->steps,
+                                             reinterpret_cast<int*>(bad), (hipStream_t)stream),
+                    "qpack_encode_nested launch");
+}
+
+qp_status qpack_concat_n(const qp_desc* d_out, int32_t parts, const qp_desc* d_in,
+                         const qp_weights* w_in, const qp_weights* out, void* stream) {
+  qp::Desc dd;
+  qp_status st = check_desc(d_out, &dd);
+  if (st != QP_OK) return st;
+  if (parts < 1) return fail(QP_EINVAL, "parts must be >= 1 (got %d)", parts);
+  if (!d_in || !w_in || !out) return fail(QP_EINVAL, "d_in, w_in and out must not be NULL");
+  if ((st = check_weights(dd, out, false)) != QP_OK) return st;
+  int64_t rows = 0;
+  for (int32_t i = 0; i < parts; ++i) {
+    qp::Desc di;
+    if ((st = check_desc(&d_in[i], &di)) != QP_OK) return st;
+    const qp_desc& a = d_in[i];
+    if (a.fmt != d_out->fmt || a.bits != d_out->bits || a.group_size != d_out->group_size ||
+        a.super_block != d_out->super_block || a.meta_dtype != d_out->meta_dtype ||
+        a.K != d_out->K)
+      return fail(QP_EINVAL, "part %d differs from d_out in format, bits, group size, "
+                  "super-block, metadata dtype or K", i);
+    if ((st = check_weights(di, &w_in[i], false)) != QP_OK) return st;
+    rows += a.N;
+  }
+  if (rows != dd.N)
+    return fail(QP_ESHAPE, "the parts' N add up to %lld, d_out has N=%lld", (long long)rows,
+                (long long)dd.N);
+  // every buffer is N-leading with a fixed byte count per row: each part's
+  // buffer lands right after the previous part's
+  size_t off[5] = {0, 0, 0, 0, 0};
+  void* dst[5] = {out->qweight, out->qweight_hi, out->scales, out->zeros, out->steps};
+  (void)hipGetLastError();
+  for (int32_t i = 0; i < parts; ++i) {
+    qp::Desc di;
+    check_desc(&d_in[i], &di);
+    size_t b[5];
+    sizes_of(di, b);
+    const void* src[5] = {w_in[i].qweight, w_in[i].qweight_hi, w_in[i].scales, w_in[i].zeros,
+                          w_in[i].steps};
+    for (int q = 0; q < 5; ++q) {
+      if (!b[q]) continue;
+      const hipError_t e = hipMemcpyAsync(static_cast<unsigned char*>(dst[q]) + off[q], src[q],
+                                          b[q], hipMemcpyDeviceToDevice, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_status(e, "qpack_concat_n copy");
+      off[q] += b[q];
+    }
+  }
+  return ok();
+}
+
 qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out, int32_t out_dtype,
                            void* stream) {
   qp::Desc dd;
@@ -383,9 +454,9 @@ qp_status qlinear_forward_static(const qp_desc* d, const void* x, int32_t x_dtyp
     if (wsb > qp::static_scratch_bytes())
       return fail(QP_EUNSUPPORTED,
                   "qlinear_forward_static: this call stages %zu bytes of activations, more than "
-                  "the library's static scratch (%zu bytes, ceil(M / 16) * 16 * K <= %zu); use "
-                  "qlinear_forward_ws with a workspace",
-                  wsb, qp::static_scratch_bytes(), qp::static_scratch_bytes() / 2);
+                  "the library's static scratch (%zu bytes: ceil(M / 16) * 16 * (2 K + 4) "
+                  "bytes at most); use qlinear_forward_ws with a workspace",
+                  wsb, qp::static_scratch_bytes());
     (void)hipGetLastError();
     const hipError_t e = qp::static_scratch(&ws);
     if (e != hipSuccess) return hip_status(e, "static scratch lookup");

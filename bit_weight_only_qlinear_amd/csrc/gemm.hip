@@ -1,7 +1,10 @@
-// qGEMM host side: activation staging (prescale exponents, fp16 fragment
-// staging for the 224-row tiles), the tiling choice and the dispatch to the
+// qGEMM host side: activation staging (fp16 fragments with the bf16
+// prescale exponents for the 224-row tiles; the exponents alone, into y,
+// for the 256-row tiles), the tiling choice and the dispatch to the
 // per-format kernel instantiations.  The kernels and their design are in
 // gemm_kernels.hpp.
+#include <algorithm>
+
 #include "gemm_kernels.hpp"
 
 namespace qp {
@@ -11,24 +14,56 @@ namespace {
 // of v_mfma_f32_16x16x32_f16.  16-byte chunk c = (mb * K/32 + kq) * 64 + l
 // holds row 16 mb + (l & 15), columns 32 kq + 8 (l >> 4) .. + 7 in the order
 // (0,4,1,5,2,6,3,7); rows from M up to the next multiple of 16 are zero.
-// bf16 rows are prescaled by their exponent (left in y by k_xexp, at the
-// row's column 0).
+// Blocks of 1024 threads: `ks` blocks per 16-row group mb, block q of them
+// converting the q-th of ks equal runs of the group's chunks (1024 is a
+// multiple of 64, so a thread's chunks all belong to one row).  For bf16
+// every block first reduces the rows' max |x| over the whole row, one wave
+// per row reading it contiguously (the group's ks blocks repeat that read,
+// from cache), to the prescale exponent
+// e = 14 - floor(log2 max|x|) (0 for an all-zero row), which scales the
+// row's peak into [2^14, 2^15) -- inside fp16's range; block 0 writes it to
+// xe[row] for the qGEMM's epilogue.
+constexpr int kStageThreads = 1024;
+
 template <bool XBF16>
-__global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x,
-                                               uint4* __restrict__ xf, uint32_t M, uint32_t K,
-                                               uint32_t nchunks, GemmArgs a) {
-  const uint32_t c = blockIdx.x * 256u + threadIdx.x;
-  if (c >= nchunks) return;
-  const uint32_t l = c & 63u, blk = c >> 6, kb = K / 32u;
-  const uint32_t mb = blk / kb, kq = blk - mb * kb;
-  const uint32_t row = 16u * mb + (l & 15u), col = 32u * kq + 8u * (l >> 4);
-  uint4 u = make_uint4(0u, 0u, 0u, 0u);
+__global__ void __launch_bounds__(kStageThreads) k_xstage(const uint16_t* __restrict__ x,
+                                                          uint4* __restrict__ xf,
+                                                          int* __restrict__ xe, uint32_t M,
+                                                          uint32_t K, uint32_t ks) {
+  __shared__ uint32_t s_max[16];
+  const uint32_t mb = blockIdx.x / ks, part = blockIdx.x % ks, tid = threadIdx.x;
+  const uint32_t nch = (K / 32u) * 64u;   // chunks of the row group
+  const uint32_t l = tid & 63u, r = l & 15u, row = 16u * mb + r;
+  const uint16_t* xr = x + (uint64_t)row * K + 8u * (l >> 4);
   int e = 0;
-  if (row < M) {
-    u = *reinterpret_cast<const uint4*>(x + (uint64_t)row * K + col);
-    if constexpr (XBF16) e = read_exp(a, row, 0);
+  if constexpr (XBF16) {
+    // wave w reduces row 16 mb + w, reading it in contiguous 1 KiB pieces
+    const uint32_t wr = tid >> 6, rrow = 16u * mb + wr;
+    uint32_t mx = 0;   // |bf16| compares as its bit pattern with the sign cleared
+    if (rrow < M) {
+      const uint4* xw = reinterpret_cast<const uint4*>(x + (uint64_t)rrow * K);
+      for (uint32_t c = l; c < K / 8u; c += 64u) {
+        const uint4 u = xw[c];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7FFFu, (w[q] >> 16) & 0x7FFFu));
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if (l == 0) s_max[wr] = mx;
+    __syncthreads();
+    const float f = bf16_to_f32(s_max[r]);
+    e = f == 0.f ? 0 : 14 - ilogbf(f);
+    if (part == 0 && tid < 16) xe[16u * mb + tid] = e;
   }
-  xf[c] = act_chunk<XBF16>(u, e);
+  // this block's run of chunks (a multiple of 1024 chunks, or the tail)
+  const uint32_t per = ((nch + kStageThreads - 1) / kStageThreads + ks - 1) / ks * kStageThreads;
+  const uint32_t j0 = part * per, j1 = min(nch, j0 + per);
+  for (uint32_t j = j0 + tid; j < j1; j += kStageThreads) {
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (row < M) u = *reinterpret_cast<const uint4*>(xr + 32u * (j >> 6));
+    xf[(uint64_t)mb * nch + j] = act_chunk<XBF16>(u, e);
+  }
 }
 
 // Prescale exponent of each bf16 activation row: e = 14 - floor(log2 of the
@@ -41,8 +76,17 @@ __global__ void __launch_bounds__(256) k_xexp(const uint16_t* __restrict__ x, in
                                               int64_t N, int ydt, int colstep, int ntiles) {
   __shared__ float wm[4];
   const int64_t m = blockIdx.x;
-  float mx = 0.f;
-  for (int64_t k = threadIdx.x; k < K; k += 256) mx = fmaxf(mx, fabsf(bf16_to_f32(x[m * K + k])));
+  // K % 64 == 0 for the qGEMM: 16-byte loads of 8 bf16; |bf16| compares as
+  // its bit pattern with the sign cleared
+  const uint4* xr = reinterpret_cast<const uint4*>(x + m * K);
+  uint32_t mb = 0;
+  for (int64_t c = threadIdx.x; c < K / 8; c += 256) {
+    const uint4 u = xr[c];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mb = max(mb, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+  }
+  float mx = bf16_to_f32(mb);
   mx = wave_max_all(mx);
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
   __syncthreads();
@@ -68,11 +112,18 @@ bool use_n224(const Desc& d, int64_t M) {
 
 }  // namespace
 
+// Staged activations (fp16 fragments), then one int32 prescale exponent per
+// staged row.
+static uint64_t staged_bytes(const Desc& d, int64_t M) {
+  return (uint64_t)cdiv(M, 16) * 16u * (uint64_t)d.K * 2u;
+}
+
 size_t gemm_workspace_bytes(const Desc& d, int64_t M) {
   if (!use_n224(d, M)) return 0;
-  const uint64_t bytes = (uint64_t)cdiv(M, 16) * 16u * (uint64_t)d.K * 2u;
-  // 32-bit chunk indices in k_xprep and 32-bit buffer offsets
-  return bytes <= (uint64_t(1) << 31) ? (size_t)bytes : 0;
+  const uint64_t bytes = staged_bytes(d, M);
+  // 32-bit buffer offsets in k_gemm224
+  if (bytes > (uint64_t(1) << 31)) return 0;
+  return (size_t)(bytes + (uint64_t)cdiv(M, 16) * 16u * 4u);
 }
 
 hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const Bufs& b,
@@ -87,6 +138,9 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.steps = b.steps;
   a.x = x;
   a.xf = n224 ? ws : nullptr;
+  a.xe = n224 ? reinterpret_cast<const int*>(static_cast<const unsigned char*>(ws) +
+                                            staged_bytes(d, M))
+              : nullptr;
   a.bias = bias;
   a.y = y;
   a.M = M;
@@ -96,20 +150,24 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.ydt = ydt;
   a.tilesM = (int)((M + BM - 1) / BM);
   a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
-  if (xdt == BF16)   // per-row prescale exponents into y (see k_xexp)
-    hipLaunchKernelGGL(k_xexp, dim3((unsigned)M), dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       d.K, y, d.N, ydt, n224 ? BN7 : BN, a.tilesN);
-  if (n224) {
-    const uint32_t nchunks = (uint32_t)(wsb / 16u);
-    const unsigned xblocks = (nchunks + 255u) / 256u;
+  if (n224) {   // staging (with the bf16 prescale exponents) into the workspace
+    int* xe = const_cast<int*>(a.xe);
+    // enough blocks for the chip: split each 16-row group's conversion over
+    // up to 8 blocks (each repeats the group's max pass, from cache)
+    const int64_t groups = cdiv(M, 16);
+    const uint32_t ks = (uint32_t)std::max<int64_t>(1, std::min<int64_t>(8, 512 / groups));
+    const dim3 grid((unsigned)(groups * ks));
     if (xdt == BF16)
-      hipLaunchKernelGGL(k_xprep<true>, dim3(xblocks), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
-                         (uint32_t)d.K, nchunks, a);
+      hipLaunchKernelGGL(k_xstage<true>, grid, dim3(kStageThreads), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), xe,
+                         (uint32_t)M, (uint32_t)d.K, ks);
     else
-      hipLaunchKernelGGL(k_xprep<false>, dim3(xblocks), dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), (uint32_t)M,
-                         (uint32_t)d.K, nchunks, a);
+      hipLaunchKernelGGL(k_xstage<false>, grid, dim3(kStageThreads), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), xe,
+                         (uint32_t)M, (uint32_t)d.K, ks);
+  } else if (xdt == BF16) {   // per-row prescale exponents into y (see k_xexp)
+    hipLaunchKernelGGL(k_xexp, dim3((unsigned)M), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       d.K, y, d.N, ydt, BN, a.tilesN);
   }
   const unsigned blocks = (unsigned)a.tilesM * (unsigned)a.tilesN;
   GemmPick p;

@@ -65,7 +65,8 @@ struct GemmArgs {
   const void* zeros;
   const void* steps;
   const void* x;
-  const void* xf;   // activations staged by k_xprep (k_gemm224), else null
+  const void* xf;   // activations staged by k_xstage (k_gemm224), else null
+  const int* xe;    // their prescale exponents (bf16, k_gemm224), else null
   const void* bias;
   void* y;
   int64_t M, N, K;
@@ -125,9 +126,9 @@ template <> struct GT<G_AFF2> { static constexpr int W = 4, H = 0; };
 template <> struct GT<G_AFF8> { static constexpr int W = 16, H = 0; };
 template <> struct GT<G_Q6K> { static constexpr int W = 8, H = 4; };
 
-// Prescale exponent of activation row m, as the exponent kernel left it in
-// y at (m, c): the first column of each n-tile of the row.  Only the block
-// of that tile reads it, before it writes the tile.
+// Prescale exponent of activation row m for the 256-row tiling, as the
+// exponent kernel left it in y at (m, c): the first column of each n-tile of
+// the row.  Only the block of that tile reads it, before it writes the tile.
 __device__ __forceinline__ int read_exp(const GemmArgs& a, int64_t m, int64_t c) {
   const int64_t i = m * a.N + c;
   return a.ydt == F32 ? static_cast<const int*>(a.y)[i]
@@ -622,7 +623,7 @@ k_gemm(GemmArgs a) {
 // 7/8 the work each.  A wave then owns 112 weight rows, not a multiple of
 // 32, so this kernel runs v_mfma_f32_16x16x32_f16: 7 x 4 tiles of 16 x 16
 // per wave (wave grid 2 (n) x 4 (m) as in k_gemm).  The activations are
-// staged once per call by k_xprep as fp16 in that MFMA's B-fragment order,
+// staged once per call by k_xstage as fp16 in that MFMA's B-fragment order,
 // and each wave loads its B fragments straight into registers, one step
 // ahead; only the weight tile goes through LDS, staged, swizzled and
 // dequantized as in k_gemm (rows 224..255 of the LDS tile are unused).
@@ -882,7 +883,7 @@ k_gemm224(GemmArgs a) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) st_w(0u, p, weight_chunk<KIND, MBF16>(st0, p, magic));
   if constexpr (XBF16) {
-    if (tid < BM) s_xe[tid] = m0 + tid < a.M ? read_exp(a, m0 + tid, n0) : 0;
+    if (tid < BM) s_xe[tid] = m0 + tid < a.M ? a.xe[m0 + tid] : 0;
   }
   __syncthreads();
   if constexpr (MCH) {

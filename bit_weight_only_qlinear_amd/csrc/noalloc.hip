@@ -17,7 +17,7 @@
 namespace qp {
 namespace {
 
-constexpr size_t kScratchBytes = size_t(32) << 20;   // 32 MiB per GPU
+constexpr size_t kScratchBytes = size_t(40) << 20;   // 40 MiB per GPU
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

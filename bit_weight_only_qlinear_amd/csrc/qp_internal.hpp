@@ -58,6 +58,10 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M,
                        const Bufs& b, const void* bias, void* y, int ydt,
                        void* ws, hipStream_t s);
 
+// Plain per-group metadata (fp32 scales, Q4K zero points) into the nested
+// Q4K / Q6K metadata buffers; *bad (optional, device) flags invalid inputs.
+hipError_t launch_encode_nested(const Desc& d, const float* sv, const float* zv, void* scales,
+                                void* zeros, void* steps, int* bad, hipStream_t st);
 // Per-token symmetric int8 activations: q [M, K] int8, s [M] fp32.
 hipError_t launch_quant_act(const void* x, int xdt, int64_t M, int64_t K, void* q, float* s,
                             hipStream_t st);

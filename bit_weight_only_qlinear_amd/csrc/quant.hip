@@ -376,36 +376,124 @@ inline unsigned blocks_for(int64_t n) {
   return (unsigned)((n + kThreads - 1) / kThreads);
 }
 
+// ------------------------------------------------- nested re-encoding
+// Plain per-group metadata into the nested superscale form (ExecuTorch PR
+// #20571: the original int4 / int6 tensors are converted into Q4_K / Q6_K,
+// codes unchanged, only the metadata re-quantized).  One thread per
+// super-block of 256, the rule of the nested quantizers' second stage:
+// step = fp16(fl32(max / levels)), code = step == 0 ? 0 :
+// clamp(rint(fl32(v / step)), 0, code_max).  A negative or non-finite input
+// sets *bad (when given) and is encoded as if it were 0.
+__device__ __forceinline__ float plain_in(float v, int* bad) {
+  if (!(v >= 0.f) || !(v <= 3.402823466e38f)) {
+    if (bad) atomicOr(bad, 1);
+    return 0.f;
+  }
+  return v;
+}
+
+template <int G, int LEVELS>
+__device__ __forceinline__ uint32_t encode_super(const float* v, uint8_t* codes, int* bad) {
+  float x[G];
+  float mx = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    x[g] = plain_in(v[g], bad);
+    mx = fmaxf(mx, x[g]);
+  }
+  const uint32_t bits = f32_to_f16_rne(div_rn(mx, (float)LEVELS));
+  const float step = f16_to_f32(bits);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+    codes[g] = (uint8_t)(step == 0.f ? 0.f : clampf(rintf(div_rn(x[g], step)), 0.f, (float)LEVELS));
+  return bits;
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_encode_q4k(const float* __restrict__ s, const float* __restrict__ z, uint8_t* __restrict__ sc,
+             uint8_t* __restrict__ zc, uint32_t* __restrict__ steps, int64_t nsb, int* bad) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nsb) return;   // super-block t: groups 8 t .. 8 t + 7 of the [N, K/32] arrays
+  const uint32_t sb = encode_super<8, 255>(s + 8 * t, sc + 8 * t, bad);
+  const uint32_t zb = encode_super<8, 255>(z + 8 * t, zc + 8 * t, bad);
+  steps[t] = sb | (zb << 16);
+}
+
+__global__ void __launch_bounds__(kThreads)
+k_encode_q6k(const float* __restrict__ s, int8_t* __restrict__ sc, uint16_t* __restrict__ steps,
+             int64_t nsb, int* bad) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nsb) return;   // super-block t: groups 16 t .. 16 t + 15 of [N, K/16]
+  steps[t] = (uint16_t)encode_super<16, 127>(s + 16 * t, reinterpret_cast<uint8_t*>(sc + 16 * t),
+                                             bad);
+}
+
 // Per-token symmetric int8 activations (the "a8" of ExecuTorch PR #16577,
 // "Arm backend: Support a8w4 for convolution and linear"; the page leaves
 // the rule open, the one taken is per row m):
 //   s_m = fl32(max_k |x[m, k]| / 127),
 //   q[m, k] = s_m == 0 ? 0 : clamp(rint(fl32(x[m, k] / s_m)), -127, 127).
-// One block per row; every step the single IEEE operation written above.
+// One block of 1024 threads per row, 8 elements per thread and pass (16-byte
+// loads, 8-byte stores) when K % 8 == 0, else one element; the second pass
+// re-reads the row from cache.  Every step the single IEEE operation above.
+constexpr int kActThreads = 1024;
+
 template <bool XBF16>
-__global__ void __launch_bounds__(kThreads)
+__device__ __forceinline__ float act_val(uint32_t b) {
+  return XBF16 ? bf16_to_f32(b) : f16_to_f32(b);
+}
+
+template <bool XBF16>
+__device__ __forceinline__ int8_t act_code(float v, float sc) {
+  return (int8_t)(int)(sc == 0.f ? 0.f : clampf(rintf(div_rn(v, sc)), -127.f, 127.f));
+}
+
+template <bool XBF16>
+__global__ void __launch_bounds__(kActThreads)
 k_quant_act(const uint16_t* __restrict__ x, int64_t K, int8_t* __restrict__ q, float* __restrict__ s) {
-  __shared__ float wmax[kThreads / 64];
+  __shared__ float wmax[kActThreads / 64];
   const int64_t m = blockIdx.x;
   const uint16_t* xr = x + m * K;
+  int8_t* qr = q + m * K;
+  const bool vec = (K & 7) == 0;
   float amax = 0.f;
-  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
-    const uint32_t b = xr[k];
-    amax = fmaxf(amax, fabsf(XBF16 ? bf16_to_f32(b) : f16_to_f32(b)));
+  if (vec) {
+    for (int64_t c = threadIdx.x; c < K / 8; c += kActThreads) {
+      const uint4 u = reinterpret_cast<const uint4*>(xr)[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(act_val<XBF16>(w[e] & 0xFFFFu)),
+                                 fabsf(act_val<XBF16>(w[e] >> 16))));
+    }
+  } else {
+    for (int64_t k = threadIdx.x; k < K; k += kActThreads)
+      amax = fmaxf(amax, fabsf(act_val<XBF16>(xr[k])));
   }
   amax = wave_max_all(amax);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = wmax[0];
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
+  for (int w = 1; w < kActThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
   const float sc = div_rn(amax, 127.f);
   if (threadIdx.x == 0) s[m] = sc;
-  for (int64_t k = threadIdx.x; k < K; k += kThreads) {
-    const uint32_t b = xr[k];
-    const float v = XBF16 ? bf16_to_f32(b) : f16_to_f32(b);
-    const float c = sc == 0.f ? 0.f : clampf(rintf(div_rn(v, sc)), -127.f, 127.f);
-    q[m * K + k] = (int8_t)(int)c;
+  if (vec) {
+    for (int64_t c = threadIdx.x; c < K / 8; c += kActThreads) {
+      const uint4 u = reinterpret_cast<const uint4*>(xr)[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      uint32_t o[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (uint8_t)act_code<XBF16>(act_val<XBF16>(w[e] & 0xFFFFu), sc);
+        const uint32_t hi = (uint8_t)act_code<XBF16>(act_val<XBF16>(w[e] >> 16), sc);
+        o[e >> 1] |= (lo | (hi << 8)) << (16 * (e & 1));
+      }
+      reinterpret_cast<uint2*>(qr)[c] = make_uint2(o[0], o[1]);
+    }
+  } else {
+    for (int64_t k = threadIdx.x; k < K; k += kActThreads)
+      qr[k] = act_code<XBF16>(act_val<XBF16>(xr[k]), sc);
   }
 }
 
@@ -476,11 +564,24 @@ hipError_t launch_dequant(const Desc& d, const Bufs& b, void* out, int out_dt, h
 hipError_t launch_quant_act(const void* x, int xdt, int64_t M, int64_t K, void* q, float* s,
                             hipStream_t st) {
   if (xdt == BF16)
-    hipLaunchKernelGGL(k_quant_act<true>, dim3((unsigned)M), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(k_quant_act<true>, dim3((unsigned)M), dim3(kActThreads), 0, st,
                        static_cast<const uint16_t*>(x), K, static_cast<int8_t*>(q), s);
   else
-    hipLaunchKernelGGL(k_quant_act<false>, dim3((unsigned)M), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(k_quant_act<false>, dim3((unsigned)M), dim3(kActThreads), 0, st,
                        static_cast<const uint16_t*>(x), K, static_cast<int8_t*>(q), s);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_nested(const Desc& d, const float* sv, const float* zv, void* scales,
+                                void* zeros, void* steps, int* bad, hipStream_t st) {
+  const int64_t nsb = d.N * (d.K / 256);   // super-blocks: one step word / step each
+  if (d.fmt == Q4K)
+    hipLaunchKernelGGL(k_encode_q4k, dim3(blocks_for(nsb)), dim3(kThreads), 0, st, sv, zv,
+                       static_cast<uint8_t*>(scales), static_cast<uint8_t*>(zeros),
+                       static_cast<uint32_t*>(steps), nsb, bad);
+  else
+    hipLaunchKernelGGL(k_encode_q6k, dim3(blocks_for(nsb)), dim3(kThreads), 0, st, sv,
+                       static_cast<int8_t*>(scales), static_cast<uint16_t*>(steps), nsb, bad);
   return hipGetLastError();
 }
 

@@ -1,18 +1,20 @@
-// Skinny MFMA qGEMV for small activation batches (M <= 16 per block row of
-// activations, any M in tiles of 16): y = x W^T on exact codes.
+// Skinny MFMA qGEMV for small activation batches (up to 16 activation rows
+// per block, any M in tiles of 16): y = x W^T on exact codes.
 //
-// The activation rows ride in the 16 columns of v_mfma_f32_16x16x32_{bf16,
-// f16}; the A operand is 16 weight rows x 32 columns of *codes*, each held
-// exactly as MAG + u (MAG = 128 in bf16 for 2-, 4- and 6-bit codes, 1024 in
-// fp16; 8-bit codes with bf16 activations are held as u itself, MAG = 0), so
-// every product code x activation is exact and the sums are fp32.  The
-// group's scale and offset are applied once per (weight row, group) in fp32
-// after the group's MFMAs (the superscale page's factorisation
+// v_mfma_f32_16x16x32_{bf16,f16} with the activation rows as the A operand
+// (16 rows x 32 columns) and the *codes* of 16 weight rows as the B operand,
+// each code held exactly as MAG + u (MAG = 128 in bf16 for 2-, 4- and 6-bit
+// codes, 1024 in fp16; 8-bit codes with bf16 activations are held as u
+// itself, MAG = 0), so every product code x activation is exact and the sums
+// are fp32.  A lane's accumulators then hold 4 activation rows of ONE weight
+// row, so the group's scale and offset are one register pair per lane,
+// applied once per (weight row, group) in fp32 after the group's MFMAs (the
+// superscale page's factorisation
 //     sum_k w_k x_k = S * sum (MAG + u) x + T * sum x
 // with AFFINE S = scale, T = bias - MAG * scale; Q4K S = sc*sstep,
 // T = -S * (MAG + zc*zstep); Q6K S = sc*step, T = -S * (MAG + 32); SYM4
 // S = scale, T = -S * (MAG + 8)).  sum x of the group comes from one more
-// MFMA per step with A = 1.  Activations are used in their own type: bf16
+// MFMA per step with B = 1.  Activations are used in their own type: bf16
 // stays bf16, fp16 stays fp16 -- no range limit beyond the type's own.
 //
 // Group-pure MFMA steps.  A lane loads 16 contiguous bytes of a weight row
@@ -26,9 +28,13 @@
 //
 // Work split: a block owns 32 weight rows (two 16-row tiles) and 16
 // activation rows (blockIdx.y); its 8 waves take every 8th 128-column block
-// of K, one block's loads in flight ahead of the one computed, and their
-// partial sums meet in LDS.  Each wave turns its block's metadata into fp32
-// (S, T) per (row, group) once, in its own LDS slice.
+// of K, kSxStages - 1 blocks' loads in flight ahead of the one computed, and
+// their partial sums meet in LDS.  The metadata of the block's 32 rows is
+// one contiguous slab per array (rows are N-leading); the block first copies
+// the slabs into LDS with 16-byte loads (when they fit in 64 KiB) and each
+// lane then reads its rows' few bytes per column block from there.  Small
+// per-lane loads straight from HBM, 16 rows per instruction, cost more than
+// the codes themselves; they remain only for rows too long for LDS.
 //
 // Sources: HF Transformers "Metal" page (uint32 codes, per-group scale and
 // bias, bits 2/4/8); ExecuTorch PR #20571 "Quant schema update" (Q4_K/Q6_K-
@@ -45,8 +51,16 @@ namespace {
 enum SxKind : int { S_AFF2 = 0, S_AFF4 = 1, S_AFF8 = 2, S_Q4K = 3, S_Q6K = 4, S_SYM4 = 5 };
 
 constexpr int kSxRows = 32;     // weight rows per block
-constexpr int kSxWaves = 8;     // K splits per block
+#ifndef QP_SX_WAVES
+#define QP_SX_WAVES 8
+#endif
+constexpr int kSxWaves = QP_SX_WAVES;   // K splits per block
+static_assert(kSxWaves >= 8, "the final sum maps 512 threads to 32 x 16 outputs");
 constexpr int kSxCols = 128;    // columns per block step
+#ifndef QP_SX_STAGES
+#define QP_SX_STAGES 2
+#endif
+constexpr int kSxStages = QP_SX_STAGES;   // register stages (kSxStages - 1 loads ahead)
 constexpr uint32_t kOOB = 0x80000000u;
 
 struct SxArgs {
@@ -57,10 +71,14 @@ struct SxArgs {
   const void* bias;
   void* y;
   int64_t M, N, K;
-  int gs, ydt;
+  int ydt;
   uint32_t qw_bytes, qh_bytes, x_bytes;
   uint32_t meta_bytes[3];   // allocated sizes (16-byte multiples)
+  uint32_t meta_row[3];     // bytes per weight row of each metadata array
+  uint32_t meta_lds[3];     // LDS offset of each array's slab (LDSM)
 };
+
+constexpr uint32_t kSxMetaLds = 64u << 10;   // LDS budget for the metadata slabs
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -71,6 +89,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
                                            0x00020000);
 }
 
+// D += A B with A the activations, B the codes.
 template <bool XBF16>
 __device__ __forceinline__ float4_t mfma(uint4 a, uint4 b, float4_t c) {
   if constexpr (XBF16)
@@ -105,22 +124,64 @@ constexpr int code_bits(int k) { return k == S_AFF2 ? 2 : k == S_AFF8 ? 8 : 4; }
 // Magic offset held in every code element.
 template <int KIND, bool XBF16>
 constexpr float mag() { return KIND == S_AFF8 && XBF16 ? 0.f : (XBF16 ? 128.f : 1024.f); }
+// Metadata words per lane and tile of one 128-column block.
+template <int KIND, int GS>
+constexpr int meta_words() {
+  return KIND == S_Q4K || KIND == S_Q6K ? 2
+       : KIND == S_SYM4 ? 128 / (GS > 0 ? GS : 128)
+       : 4;   // AFFINE: scales in words 0-1, biases in words 2-3
+}
 
 // One lane's raw data of one 128-column block.
-template <int KIND>
+template <int KIND, int GS>
 struct SxStage {
-  // codes of the lane's two rows (tiles i = 0, 1), 32 columns each:
+  // codes of the lane's row in each tile i = 0, 1, 32 columns each:
   // int2 2 words, int4 4, int8 8; Q6K 4 low-nibble words + 2 high-bit words
-  uint32_t w[2][code_bits(KIND) * 32 / 32];
+  uint32_t w[2][code_bits(KIND)];
   uint32_t h[2][KIND == S_Q6K ? 2 : 1];
   uint4 x[4];            // activations, 8 columns per MFMA step
-  uint2 m;               // the lane's share of the block's metadata
-  uint32_t st;           // Q4K / Q6K step (per 256 columns)
+  uint32_t m[2][meta_words<KIND, GS>()];
+  uint32_t st[2];        // Q4K step word / Q6K fp16 step (per 256 columns)
 };
 
-template <int KIND, bool PERCH>
-__device__ __forceinline__ void sx_load(const SxArgs& a, int kb, int lane, int64_t n0,
-                                        int64_t mrow, SxStage<KIND>& s) {
+// Metadata word(s) of `bytes` bytes (2, 4, 8 or 16) at byte `off` of array q
+// for row n: from the LDS slab (row n - n0) or from HBM.
+template <bool LDSM, int BYTES>
+__device__ __forceinline__ void meta_ld(const SxArgs& a, const unsigned char* lds, int q,
+                                        __amdgpu_buffer_rsrc_t r, bool ok, uint32_t row_local,
+                                        uint32_t row_global, uint32_t off, uint32_t* dst) {
+  if constexpr (LDSM) {
+    const unsigned char* p = lds + a.meta_lds[q] + row_local * a.meta_row[q] + off;
+    if constexpr (BYTES == 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p);
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    } else if constexpr (BYTES == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      dst[0] = v.x; dst[1] = v.y;
+    } else if constexpr (BYTES == 4) {
+      dst[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      dst[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  } else {
+    const uint32_t o = ok ? row_global * a.meta_row[q] + off : kOOB;
+    if constexpr (BYTES == 16) {
+      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    } else if constexpr (BYTES == 8) {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0));
+      dst[0] = v.x; dst[1] = v.y;
+    } else if constexpr (BYTES == 4) {
+      dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+    } else {
+      dst[0] = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, 0);
+    }
+  }
+}
+
+template <int KIND, int GS, bool LDSM>
+__device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* lds, int kb, int lane,
+                                        int64_t n0, int64_t mrow, SxStage<KIND, GS>& s) {
   const uint32_t c0 = (uint32_t)kb * kSxCols;
   const int g = lane >> 4, r16 = lane & 15;
   const uint32_t K = (uint32_t)a.K;
@@ -131,16 +192,19 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, int kb, int lane, int64
   for (int t = 0; t < 4; ++t)
     s.x[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rx, xo == kOOB ? kOOB : xo + 64u * t, 0, 0));
-  // codes: row n0 + 16 i + r16, columns c0 + 32 g .. + 32
-  const __amdgpu_buffer_rsrc_t rq = rsrc(a.qw, a.qw_bytes);
   constexpr uint32_t B = code_bits(KIND);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(a.qw, a.qw_bytes);
+  const __amdgpu_buffer_rsrc_t r0 = rsrc(a.meta[0], a.meta_bytes[0]);
+  const __amdgpu_buffer_rsrc_t r1 = rsrc(a.meta[1], a.meta_bytes[1]);
+  const __amdgpu_buffer_rsrc_t r2 = rsrc(a.meta[2], a.meta_bytes[2]);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
+    // codes: row n0 + 16 i + r16, columns c0 + 32 g .. + 32
     const int64_t n = n0 + 16 * i + r16;
     const bool ok = n < a.N;
     const uint32_t off = ok ? (uint32_t)n * (K * B / 8u) + (c0 + 32u * g) * B / 8u : kOOB;
     if constexpr (B == 2) {
-      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0));
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 2));
       s.w[i][0] = v.x; s.w[i][1] = v.y;
     } else {
 #pragma unroll
@@ -156,47 +220,27 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, int kb, int lane, int64
       const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rh, ho, 0, 2));
       s.h[i][0] = v.x; s.h[i][1] = v.y;
     }
-  }
-  // metadata: lane -> block row rr = lane >> 1, half hh = lane & 1
-  const int rr = lane >> 1, hh = lane & 1;
-  const int64_t n = n0 + rr;
-  s.m = make_uint2(0, 0);
-  s.st = 0;
-  if (n >= a.N) return;
-  if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
-    // hh = 0: scales, hh = 1: biases; 128 / gs groups of 2 bytes
-    const uint32_t ng = 128u / (uint32_t)a.gs;
-    const uint32_t off = (uint32_t)n * (K / (uint32_t)a.gs) * 2u + (c0 / (uint32_t)a.gs) * 2u;
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.meta[hh], a.meta_bytes[hh]);
-    if (ng == 4)
-      s.m = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    else if (ng == 2)
-      s.m.x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    else
-      s.m.x = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  } else if constexpr (KIND == S_Q4K) {
-    // hh = 0: 4 scale codes, hh = 1: 4 zero codes; both: the step word
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.meta[hh], a.meta_bytes[hh]);
-    s.m.x = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)n * (K / 32u) + c0 / 32u, 0, 0);
-    s.st = __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.meta[2], a.meta_bytes[2]),
-                                                (uint32_t)n * (K / 256u) * 4u + (c0 / 256u) * 4u, 0, 0);
-  } else if constexpr (KIND == S_Q6K) {
-    // hh: 4 of the block's 8 int8 scale codes; both: the fp16 step
-    s.m.x = __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.meta[0], a.meta_bytes[0]),
-                                                 (uint32_t)n * (K / 16u) + c0 / 16u + 4u * hh, 0, 0);
-    s.st = __builtin_amdgcn_raw_buffer_load_b16(rsrc(a.meta[2], a.meta_bytes[2]),
-                                                (uint32_t)n * (K / 256u) * 2u + (c0 / 256u) * 2u, 0, 0);
-  } else if constexpr (!PERCH) {
-    // SYM4 per group: 128 / gs fp32 scales; hh takes half of them
-    const uint32_t ng = 128u / (uint32_t)a.gs;
-    const uint32_t off = (uint32_t)n * (K / (uint32_t)a.gs) * 4u + (c0 / (uint32_t)a.gs) * 4u;
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.meta[0], a.meta_bytes[0]);
-    if (ng == 4)
-      s.m = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 8u * hh, 0, 0));
-    else if (ng == 2)
-      s.m.x = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4u * hh, 0, 0);
-    else if (hh == 0)
-      s.m.x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    // metadata of row n for the block's groups (rows past N read 0)
+    const uint32_t rl = (uint32_t)(16 * i + r16), rg = (uint32_t)n;
+    if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
+      // 128 / GS groups of 2 bytes: scales into m[0..1], biases into m[2..3]
+      constexpr int MB = 256 / GS;
+      s.m[i][1] = s.m[i][3] = 0;
+      meta_ld<LDSM, MB>(a, lds, 0, r0, ok, rl, rg, (c0 / GS) * 2u, &s.m[i][0]);
+      meta_ld<LDSM, MB>(a, lds, 1, r1, ok, rl, rg, (c0 / GS) * 2u, &s.m[i][2]);
+    } else if constexpr (KIND == S_Q4K) {
+      // 4 uint8 scale codes, 4 uint8 zero codes, the step word
+      meta_ld<LDSM, 4>(a, lds, 0, r0, ok, rl, rg, c0 / 32u, &s.m[i][0]);
+      meta_ld<LDSM, 4>(a, lds, 1, r1, ok, rl, rg, c0 / 32u, &s.m[i][1]);
+      meta_ld<LDSM, 4>(a, lds, 2, r2, ok, rl, rg, (c0 / 256u) * 4u, &s.st[i]);
+    } else if constexpr (KIND == S_Q6K) {
+      // 8 int8 scale codes, the fp16 step
+      meta_ld<LDSM, 8>(a, lds, 0, r0, ok, rl, rg, c0 / 16u, &s.m[i][0]);
+      meta_ld<LDSM, 2>(a, lds, 2, r2, ok, rl, rg, (c0 / 256u) * 2u, &s.st[i]);
+    } else if constexpr (GS > 0) {
+      // SYM4 per group: 128 / GS fp32 scales
+      meta_ld<LDSM, 512 / GS>(a, lds, 0, r0, ok, rl, rg, (c0 / GS) * 4u, &s.m[i][0]);
+    }
   }
 }
 
@@ -204,7 +248,7 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, int kb, int lane, int64
 // 0 and 2: codes 0-3 in byte 0, codes 4-7 in byte 2 (2 bits each).
 __device__ __forceinline__ uint32_t spread2(uint32_t p) { return (p & 0xFFu) | ((p & 0xFF00u) << 8); }
 
-// A operand of one MFMA step: the lane's 8 codes in element order
+// B operand of one MFMA step: the lane's 8 codes in element order
 // (0, 4, 1, 5, 2, 6, 3, 7), each MAG + u exactly.
 template <int KIND, bool XBF16>
 __device__ __forceinline__ uint4 code_frag(uint32_t w, uint32_t w2, uint32_t hq) {
@@ -240,7 +284,7 @@ __device__ __forceinline__ uint4 code_frag(uint32_t w, uint32_t w2, uint32_t hq)
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
-// B operand: 8 activations (two per word, column order) in the same element
+// A operand: 8 activations (two per word, column order) in the same element
 // order as code_frag.
 __device__ __forceinline__ uint4 act_frag(uint4 v) {
   return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),   // (x0, x4)
@@ -253,171 +297,168 @@ __device__ __forceinline__ float meta_f(uint32_t bits, bool bf) {
   return bf ? bf16_to_f32(bits) : f16_to_f32(bits);
 }
 
-template <int KIND, bool XBF16, bool MBF16, bool PERCH>
+// (S, T) of group gg (a compile-time constant) of the block for the lane's
+// row of tile i.
+template <int KIND, int GS, bool MBF16>
+__device__ __forceinline__ void group_st(const SxStage<KIND, GS>& s, int i, int gg, float mg,
+                                         float& S, float& T) {
+  if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
+    const uint32_t sh = 16u * (uint32_t)(gg & 1);
+    S = meta_f((s.m[i][gg >> 1] >> sh) & 0xFFFFu, MBF16);
+    T = fmaf(-mg, S, meta_f((s.m[i][2 + (gg >> 1)] >> sh) & 0xFFFFu, MBF16));
+  } else if constexpr (KIND == S_Q4K) {
+    const float sc = (float)((s.m[i][0] >> (8 * gg)) & 0xFFu);
+    const float zc = (float)((s.m[i][1] >> (8 * gg)) & 0xFFu);
+    S = sc * f16_to_f32(s.st[i] & 0xFFFFu);
+    T = -S * (mg + zc * f16_to_f32(s.st[i] >> 16));
+  } else if constexpr (KIND == S_Q6K) {
+    const float sc = (float)(int)(int8_t)((s.m[i][gg >> 2] >> (8 * (gg & 3))) & 0xFFu);
+    S = sc * f16_to_f32(s.st[i] & 0xFFFFu);
+    T = -S * (mg + 32.f);
+  } else {
+    S = __uint_as_float(s.m[i][gg]);
+    T = -S * (mg + 8.f);
+  }
+}
+
+// KIND / GS: format and group size (affine 32, 64, 128; Q4K 32; Q6K 16;
+// SYM4 32, 64, 128, or 0 for one scale per output channel, applied once to
+// the total).
+template <int KIND, int GS, bool XBF16, bool MBF16, bool LDSM>
 __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
-  // per wave: S and T of the current block, [S/T][group in block][row]
-  __shared__ __attribute__((aligned(16))) float s_st[kSxWaves][2][8][kSxRows];
-  // partial sums [wave][tile][weight row][activation row]
+  // partial sums [wave][tile][activation row][weight row]
   __shared__ float s_part[kSxWaves][2][16][17];
+  extern __shared__ __attribute__((aligned(16))) unsigned char s_meta[];   // LDSM slabs
 
   constexpr float MAG = mag<KIND, XBF16>();
+  constexpr bool PERCH = KIND == S_SYM4 && GS == 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
   const int64_t n0 = (int64_t)blockIdx.x * kSxRows;
-  const int64_t mrow = (int64_t)blockIdx.y * 16 + r16;   // this lane's activation row (B column)
+  const int64_t mrow = (int64_t)blockIdx.y * 16 + r16;   // this lane's activation row (A row)
   const int KB = (int)(a.K / kSxCols);
-  const int gs = KIND == S_Q6K ? 16 : (KIND == S_Q4K ? 32 : a.gs);
 
   const uint32_t one = XBF16 ? 0x3F803F80u : 0x3C003C00u;
   const uint4 ONES = make_uint4(one, one, one, one);
+  // acc[i][v]: activation row 4 g + v, weight row 16 i + r16
   float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float4_t D[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float4_t DX = {0.f, 0.f, 0.f, 0.f};
-  float4_t Dh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // Q6K: second group of a step
-  float4_t DXh = {0.f, 0.f, 0.f, 0.f};
 
-  // the block's metadata of one 128-column block -> (S, T) in s_st[wave]
-  auto stage_meta = [&](const SxStage<KIND>& s) {
-    const int rr = lane >> 1, hh = lane & 1;
-    if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
-      const int ng = 128 / gs;
-      // partner lane (hh ^ 1) holds the other array of the same row
-      const uint32_t ox = (uint32_t)__builtin_amdgcn_mov_dpp((int)s.m.x, 0xB1, 0xF, 0xF, false);
-      const uint32_t oy = (uint32_t)__builtin_amdgcn_mov_dpp((int)s.m.y, 0xB1, 0xF, 0xF, false);
-      const uint32_t sw[2] = {hh ? ox : s.m.x, hh ? oy : s.m.y};   // scales
-      const uint32_t bw[2] = {hh ? s.m.x : ox, hh ? s.m.y : oy};   // biases
-      for (int gg = hh; gg < ng; gg += 2) {
-        const uint32_t sb = (sw[gg >> 1] >> (16 * (gg & 1))) & 0xFFFFu;
-        const uint32_t bb = (bw[gg >> 1] >> (16 * (gg & 1))) & 0xFFFFu;
-        const float S = meta_f(sb, MBF16);
-        s_st[wave][0][gg][rr] = S;
-        s_st[wave][1][gg][rr] = fmaf(-MAG, S, meta_f(bb, MBF16));
-      }
-    } else if constexpr (KIND == S_Q4K) {
-      const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)s.m.x, 0xB1, 0xF, 0xF, false);
-      const uint32_t sc = hh ? o : s.m.x, zc = hh ? s.m.x : o;
-      const float sstep = f16_to_f32(s.st & 0xFFFFu), zstep = f16_to_f32(s.st >> 16);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int gg = 2 * q + hh;
-        const float S = (float)((sc >> (8 * gg)) & 0xFFu) * sstep;
-        const float Z = (float)((zc >> (8 * gg)) & 0xFFu) * zstep;
-        s_st[wave][0][gg][rr] = S;
-        s_st[wave][1][gg][rr] = -S * (MAG + Z);
-      }
-    } else if constexpr (KIND == S_Q6K) {
-      const float step = f16_to_f32(s.st & 0xFFFFu);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int gg = 4 * hh + q;
-        const float S = (float)(int)(int8_t)((s.m.x >> (8 * q)) & 0xFFu) * step;
-        s_st[wave][0][gg][rr] = S;
-        s_st[wave][1][gg][rr] = -S * (MAG + 32.f);
-      }
-    } else if constexpr (!PERCH) {
-      const int ng = 128 / gs;
-      for (int q = 0; q < 2; ++q) {
-        const int gg = (ng == 4 ? 2 * hh : hh) + q;
-        if (gg < ng && (ng == 4 || q == 0)) {
-          const float S = __uint_as_float(q ? s.m.y : s.m.x);
-          s_st[wave][0][gg][rr] = S;
-          s_st[wave][1][gg][rr] = -S * (MAG + 8.f);
-        }
-      }
-    }
-  };
-
-  // group gg of the current block is complete for D, DX: apply its (S, T)
-  auto epilogue = [&](int gg, const float4_t (&Dd)[2], const float4_t& DXd) {
+  // group gg of the block is complete in Dd, DXd: apply its (S, T)
+  auto epilogue = [&](const SxStage<KIND, GS>& s, int gg, const float4_t (&Dd)[2],
+                      const float4_t& DXd) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float4_t S = *reinterpret_cast<const float4_t*>(&s_st[wave][0][gg][16 * i + 4 * g]);
-      const float4_t T = *reinterpret_cast<const float4_t*>(&s_st[wave][1][gg][16 * i + 4 * g]);
+      float S, T;
+      group_st<KIND, GS, MBF16>(s, i, gg, MAG, S, T);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][v] = fmaf(T[v], DXd[v], fmaf(S[v], Dd[i][v], acc[i][v]));
+      for (int v = 0; v < 4; ++v) acc[i][v] = fmaf(T, DXd[v], fmaf(S, Dd[i][v], acc[i][v]));
     }
   };
 
-  auto compute = [&](SxStage<KIND>& s) {
+  auto compute = [&](const SxStage<KIND, GS>& s) __attribute__((always_inline)) {
     // code words of both tiles, transposed so that step t is columns
-    // 32 t .. 32 t + 31 of the block
+    // 32 t .. 32 t + 31 of the block (2-bit fields: 16 bits per 8 columns;
+    // every index is a compile-time constant, so all stays in registers)
     uint32_t W[2][4], W2[2][4], H[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      if constexpr (KIND == S_AFF2 || KIND == S_Q6K) {
-        const uint32_t* src = KIND == S_AFF2 ? s.w[i] : s.h[i];
-        uint32_t p[4] = {src[0] & 0xFFFFu, src[0] >> 16, src[1] & 0xFFFFu, src[1] >> 16};
+      if constexpr (KIND == S_AFF2) {
+        uint32_t p[4] = {s.w[i][0] & 0xFFFFu, s.w[i][0] >> 16, s.w[i][1] & 0xFFFFu, s.w[i][1] >> 16};
         transpose4(p);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) (KIND == S_AFF2 ? W : H)[i][t] = p[t];
-      }
-      if constexpr (KIND == S_AFF8) {
+        for (int t = 0; t < 4; ++t) W[i][t] = p[t];
+      } else if constexpr (KIND == S_AFF8) {
         uint32_t p[4] = {s.w[i][0], s.w[i][2], s.w[i][4], s.w[i][6]};
         uint32_t q[4] = {s.w[i][1], s.w[i][3], s.w[i][5], s.w[i][7]};
         transpose4(p);
         transpose4(q);
 #pragma unroll
         for (int t = 0; t < 4; ++t) { W[i][t] = p[t]; W2[i][t] = q[t]; }
-      } else if constexpr (KIND != S_AFF2) {
+      } else {
         uint32_t p[4] = {s.w[i][0], s.w[i][1], s.w[i][2], s.w[i][3]};
         transpose4(p);
 #pragma unroll
         for (int t = 0; t < 4; ++t) W[i][t] = p[t];
       }
-    }
-    if constexpr (!PERCH) {
-      stage_meta(s);
-      // the wave reads back other lanes' S, T: wait for the writes
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      if constexpr (KIND == S_Q6K) {
+        uint32_t p[4] = {s.h[i][0] & 0xFFFFu, s.h[i][0] >> 16, s.h[i][1] & 0xFFFFu, s.h[i][1] >> 16};
+        transpose4(p);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint4 B = act_frag(s.x[t]);
+        for (int t = 0; t < 4; ++t) H[i][t] = p[t];
+      }
+    }
+    sfor<4>([&](auto TT) {
+      constexpr int t = decltype(TT)::value;
+      const uint4 A = act_frag(s.x[t]);
       if constexpr (KIND == S_Q6K) {
         // two groups per step: lane groups 0-1 (group 2 t), 2-3 (2 t + 1)
         const uint4 Z = make_uint4(0, 0, 0, 0);
-        const uint4 Bl = g < 2 ? B : Z, Bh = g < 2 ? Z : B;
+        const uint4 Al = g < 2 ? A : Z, Ah = g < 2 ? Z : A;
+        float4_t Dh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const uint4 A = code_frag<KIND, XBF16>(W[i][t], 0u, H[i][t]);
-          D[i] = mfma<XBF16>(A, Bl, D[i]);
-          Dh[i] = mfma<XBF16>(A, Bh, Dh[i]);
+          const uint4 Bq = code_frag<KIND, XBF16>(W[i][t], 0u, H[i][t]);
+          D[i] = mfma<XBF16>(Al, Bq, D[i]);
+          Dh[i] = mfma<XBF16>(Ah, Bq, Dh[i]);
         }
-        DX = mfma<XBF16>(ONES, Bl, DX);
-        DXh = mfma<XBF16>(ONES, Bh, DXh);
-        epilogue(2 * t, D, DX);
-        epilogue(2 * t + 1, Dh, DXh);
-        D[0] = D[1] = Dh[0] = Dh[1] = DX = DXh = float4_t{0.f, 0.f, 0.f, 0.f};
+        DX = mfma<XBF16>(Al, ONES, DX);
+        const float4_t DXh = mfma<XBF16>(Ah, ONES, float4_t{0.f, 0.f, 0.f, 0.f});
+        epilogue(s, 2 * t, D, DX);
+        epilogue(s, 2 * t + 1, Dh, DXh);
+        D[0] = D[1] = DX = float4_t{0.f, 0.f, 0.f, 0.f};
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-          D[i] = mfma<XBF16>(code_frag<KIND, XBF16>(W[i][t], KIND == S_AFF8 ? W2[i][t] : 0u, 0u), B, D[i]);
-        DX = mfma<XBF16>(ONES, B, DX);
+          D[i] = mfma<XBF16>(A, code_frag<KIND, XBF16>(W[i][t], KIND == S_AFF8 ? W2[i][t] : 0u, 0u),
+                             D[i]);
+        DX = mfma<XBF16>(A, ONES, DX);
         if constexpr (!PERCH) {
-          // a group ends every gs / 32 steps
-          const int spg = gs / 32;
-          if ((t + 1) % spg == 0) {
-            epilogue(t / spg, D, DX);
+          // a group ends every GS / 32 steps
+          constexpr int spg = (GS > 0 ? GS : 128) / 32;
+          if constexpr ((t + 1) % spg == 0) {
+            epilogue(s, t / spg, D, DX);
             D[0] = D[1] = DX = float4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
-    }
+    });
   };
 
-  // the wave's column blocks: wave, wave + 8, ...; one block in flight ahead
-  SxStage<KIND> st[2];
+  if constexpr (LDSM) {
+    // the block's metadata slabs (rows n0 .. n0 + 31, contiguous in each
+    // array; rows past N read 0) into LDS, 16 bytes per thread and load
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const uint32_t nb = 32u * a.meta_row[q];   // a multiple of 16
+      if (nb == 0) continue;
+      const __amdgpu_buffer_rsrc_t r = rsrc(a.meta[q], a.meta_bytes[q]);
+      const uint32_t base = (uint32_t)n0 * a.meta_row[q];
+      for (uint32_t j = 16u * (uint32_t)tid; j < nb; j += 16u * 64u * kSxWaves)
+        *reinterpret_cast<uint4*>(s_meta + a.meta_lds[q] + j) =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, base + j, 0, 0));
+    }
+    __syncthreads();
+  }
+
+  // the wave's column blocks: wave, wave + 8, ...; kSxStages - 1 ahead
+  SxStage<KIND, GS> st[kSxStages];
   const int J = wave < KB ? (KB - wave + kSxWaves - 1) / kSxWaves : 0;
-  if (J > 0) sx_load<KIND, PERCH>(a, wave, lane, n0, mrow, st[0]);
-  for (int j0 = 0; j0 < J; j0 += 2) {
-    sfor<2>([&](auto Q) {
+  sfor<kSxStages - 1>([&](auto P) {
+    constexpr int p = decltype(P)::value;
+    if (p < J) sx_load<KIND, GS, LDSM>(a, s_meta, wave + p * kSxWaves, lane, n0, mrow, st[p]);
+  });
+  for (int j0 = 0; j0 < J; j0 += kSxStages) {
+    sfor<kSxStages>([&](auto Q) {
       constexpr int q = decltype(Q)::value;
       const int j = j0 + q;
       if (j < J) {
-        if (j + 1 < J) sx_load<KIND, PERCH>(a, wave + (j + 1) * kSxWaves, lane, n0, mrow, st[(q + 1) % 2]);
+        if (j + kSxStages - 1 < J)
+          sx_load<KIND, GS, LDSM>(a, s_meta, wave + (j + kSxStages - 1) * kSxWaves, lane, n0,
+                                  mrow, st[(q + kSxStages - 1) % kSxStages]);
         compute(st[q]);
       }
     });
@@ -441,10 +482,10 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
   const int nl = tid >> 4, m = tid & 15;
   const int64_t n = n0 + nl;
   const int64_t mm = (int64_t)blockIdx.y * 16 + m;
-  if (mm < a.M && n < a.N) {
+  if (tid < 512 && mm < a.M && n < a.N) {
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kSxWaves; ++w) sum += s_part[w][nl >> 4][nl & 15][m];
+    for (int w = 0; w < kSxWaves; ++w) sum += s_part[w][nl >> 4][m][nl & 15];
     if constexpr (PERCH) sum *= static_cast<const float*>(a.meta[0])[n];
     if (a.bias) {
       const uint32_t bb = static_cast<const uint16_t*>(a.bias)[n];
@@ -459,9 +500,17 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
 
 typedef void (*SxFn)(SxArgs);
 
-template <int KIND, bool MB, bool PERCH>
-SxFn sx_pick(bool xb) {
-  return xb ? k_skinny<KIND, true, MB, PERCH> : k_skinny<KIND, false, MB, PERCH>;
+template <int KIND, int GS, bool MB>
+SxFn sx_pick(bool xb, bool lm) {
+  if (lm) return xb ? k_skinny<KIND, GS, true, MB, true> : k_skinny<KIND, GS, false, MB, true>;
+  return xb ? k_skinny<KIND, GS, true, MB, false> : k_skinny<KIND, GS, false, MB, false>;
+}
+
+template <int KIND>
+SxFn sx_affine(int gs, bool mb, bool xb, bool lm) {
+  if (gs == 32) return mb ? sx_pick<KIND, 32, true>(xb, lm) : sx_pick<KIND, 32, false>(xb, lm);
+  if (gs == 64) return mb ? sx_pick<KIND, 64, true>(xb, lm) : sx_pick<KIND, 64, false>(xb, lm);
+  return mb ? sx_pick<KIND, 128, true>(xb, lm) : sx_pick<KIND, 128, false>(xb, lm);
 }
 
 }  // namespace
@@ -484,28 +533,38 @@ hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const
   a.M = M;
   a.N = d.N;
   a.K = d.K;
-  a.gs = d.gs;
   a.ydt = ydt;
   a.qw_bytes = (uint32_t)bytes[0];
   a.qh_bytes = (uint32_t)bytes[1];
   a.x_bytes = (uint32_t)((uint64_t)M * d.K * 2);
-  for (int q = 0; q < 3; ++q) a.meta_bytes[q] = (uint32_t)((bytes[2 + q] + 15) & ~size_t(15));
+  uint32_t lds = 0;
+  for (int q = 0; q < 3; ++q) {
+    a.meta_bytes[q] = (uint32_t)((bytes[2 + q] + 15) & ~size_t(15));
+    // bytes per row: sizes are N * per-row bytes for every metadata array
+    a.meta_row[q] = (uint32_t)(bytes[2 + q] / (size_t)d.N);
+    if (d.fmt == SYM4 && d.gs == d.K && q == 0) a.meta_row[q] = 0;   // scale applied at the end
+    a.meta_lds[q] = lds;
+    lds += 32u * a.meta_row[q];
+  }
+  const bool lm = lds > 0 && lds <= kSxMetaLds;
+  if (!lm) lds = 0;
   const bool xb = xdt == BF16, mb = d.meta == BF16;
   SxFn fn = nullptr;
   if (d.fmt == AFFINE) {
-    if (d.bits == 2) fn = mb ? sx_pick<S_AFF2, true, false>(xb) : sx_pick<S_AFF2, false, false>(xb);
-    else if (d.bits == 4) fn = mb ? sx_pick<S_AFF4, true, false>(xb) : sx_pick<S_AFF4, false, false>(xb);
-    else fn = mb ? sx_pick<S_AFF8, true, false>(xb) : sx_pick<S_AFF8, false, false>(xb);
+    fn = d.bits == 2 ? sx_affine<S_AFF2>(d.gs, mb, xb, lm)
+       : d.bits == 4 ? sx_affine<S_AFF4>(d.gs, mb, xb, lm) : sx_affine<S_AFF8>(d.gs, mb, xb, lm);
   } else if (d.fmt == Q4K) {
-    fn = sx_pick<S_Q4K, false, false>(xb);
+    fn = sx_pick<S_Q4K, 32, false>(xb, lm);
   } else if (d.fmt == Q6K) {
-    fn = sx_pick<S_Q6K, false, false>(xb);
+    fn = sx_pick<S_Q6K, 16, false>(xb, lm);
   } else {
-    fn = d.gs == d.K ? sx_pick<S_SYM4, false, true>(xb) : sx_pick<S_SYM4, false, false>(xb);
+    fn = d.gs == d.K ? sx_pick<S_SYM4, 0, false>(xb, false)
+       : d.gs == 32  ? sx_pick<S_SYM4, 32, false>(xb, lm)
+       : d.gs == 64  ? sx_pick<S_SYM4, 64, false>(xb, lm) : sx_pick<S_SYM4, 128, false>(xb, lm);
   }
   const unsigned blocks = (unsigned)((d.N + kSxRows - 1) / kSxRows);
   const unsigned mtiles = (unsigned)((M + 15) / 16);
-  hipLaunchKernelGGL(fn, dim3(blocks, mtiles), dim3(64 * kSxWaves), 0, s, a);
+  hipLaunchKernelGGL(fn, dim3(blocks, mtiles), dim3(64 * kSxWaves), lds, s, a);
   return hipGetLastError();
 }
 

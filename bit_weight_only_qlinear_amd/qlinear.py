@@ -62,6 +62,8 @@ def _load():
         "qlinear_workspace_bytes": (I32, [D, I32, I64, I32, ctypes.POINTER(ctypes.c_size_t)]),
         "qlinear_forward_ws": (I32, [D, P, I32, I64, W, P, P, I32, I32, P, ctypes.c_size_t, P]),
         "qlinear_forward_static": (I32, [D, P, I32, I64, W, P, P, I32, I32, P]),
+        "qpack_encode_nested": (I32, [D, P, P, W, P, P]),
+        "qpack_concat_n": (I32, [D, I32, D, W, W, P]),
         "qpack_quantize_activations": (I32, [P, I32, I64, I64, P, P, P]),
         "qlinear_forward_a8w4": (I32, [D, P, P, I64, W, P, P, I32, P]),
     }
@@ -76,7 +78,9 @@ lib = _load()
 EXPORTED = ("qpack_abi_version", "qpack_last_error", "qpack_sizes", "qpack_quantize",
             "qpack_unpack_codes", "qpack_pack_codes", "qpack_dequantize",
             "qlinear_forward", "qlinear_forward_kernel", "qlinear_workspace_bytes",
-            "qlinear_forward_ws", "qlinear_forward_static", "qpack_quantize_activations",
+            "qlinear_forward_ws", "qlinear_forward_static", "qpack_encode_nested",
+            "qpack_concat_n",
+            "qpack_quantize_activations",
             "qlinear_forward_a8w4")
 
 
@@ -270,6 +274,36 @@ def qlinear_forward_static(desc: QDesc, x, w, out, bias=None, kernel: int = QP_K
                                       ctypes.byref(ws), _ptr(bias), _ptr(out), DTYPE_IDS[yd],
                                       kernel, _stream(x.device)))
     return out
+
+
+def concat_n(descs, weights):
+    """Stack layers of one format and K along N (qpack_concat_n): returns
+    (QDesc of the stacked layer, its buffers)."""
+    import dataclasses
+    d0 = descs[0]
+    dout = dataclasses.replace(d0, N=sum(d.N for d in descs))
+    out = alloc_weights(dout, device=weights[0]["qweight"].device)
+    n = len(descs)
+    dins = (_Desc * n)(*[d.c() for d in descs])
+    wins = (_Weights * n)(*[_wstruct(w) for w in weights])
+    _check(lib.qpack_concat_n(ctypes.byref(dout.c()), n, dins, wins, ctypes.byref(_wstruct(out)),
+                              _stream(weights[0]["qweight"].device)))
+    return dout, out
+
+
+def convert_to_nested(desc: QDesc, codes, s, z=None):
+    """Plain int4 (codes uint8 [N, K], s, z fp32 [N, K/32]) or int6 (codes
+    int8 [N, K], s fp32 [N, K/16]) -> nested Q4K / Q6K buffers with the codes
+    unchanged (qpack_pack_codes + qpack_encode_nested).  Returns (buffers,
+    bad) with bad a device int32 that is 1 if any input was invalid."""
+    import torch
+    w = alloc_weights(desc, device=codes.device)
+    _check(lib.qpack_pack_codes(ctypes.byref(desc.c()), _ptr(codes), ctypes.byref(_wstruct(w)),
+                                _stream(codes.device)))
+    bad = torch.zeros(4, dtype=torch.int32, device=codes.device)
+    _check(lib.qpack_encode_nested(ctypes.byref(desc.c()), _ptr(s), _ptr(z),
+                                   ctypes.byref(_wstruct(w)), _ptr(bad), _stream(codes.device)))
+    return w, bad
 
 
 def quantize_activations(x):

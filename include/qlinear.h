@@ -178,6 +178,41 @@ qp_status qpack_unpack_codes(const qp_desc* d, const qp_weights* w, void* codes,
 qp_status qpack_pack_codes(const qp_desc* d, const void* codes,
                            const qp_weights* out, void* stream);
 
+/* Fused-N concatenation: the layers w_in[0 .. parts-1] (descriptors d_in,
+ * same format, bits, group size, super-block, metadata dtype and K as d_out)
+ * stacked along N into `out` (d_out->N = the sum of their N), so that one
+ * forward call computes all of them (e.g. the q, k and v projections): the
+ * superscale page concatenates coalesced int4 weights along N for the same
+ * reason.  Every buffer is N-leading with a fixed byte count per row, so
+ * each part's bytes are copied right after the previous part's
+ * (hipMemcpyAsync on `stream`, device to device); `out` must not overlap the
+ * inputs.  Asynchronous like the other calls. */
+qp_status qpack_concat_n(const qp_desc* d_out, int32_t parts, const qp_desc* d_in,
+                         const qp_weights* w_in, const qp_weights* out, void* stream);
+
+/* Re-encode plain per-group metadata into the nested superscale form of
+ * `d` (QP_FMT_Q4K or QP_FMT_Q6K).  ExecuTorch PR #20571, "[cuda] Nested
+ * Superscale Quantization for CUDA Weights (int4 / int6)": the original int4
+ * and int6 tensors are converted into Q4_K / Q6_K and the k-quant pipeline
+ * reused; "Analysis": the codes stay identical to the source values and only
+ * the metadata is re-quantized.  Plain forms: int4 codes u in [0, 15] with
+ * w = (u - z) * s per group of 32; int6 codes q in [-32, 31] with w = q * s
+ * per group of 16.
+ *   s: device fp32 [N, K/32] (Q4K) or [N, K/16] (Q6K) group scales, >= 0;
+ *   z: device fp32 [N, K/32] zero points in code units, >= 0 (Q4K), NULL
+ *      for Q6K;
+ *   out: scales, steps (and zeros for Q4K) of the sizes qpack_sizes gives;
+ *      qweight / qweight_hi are not touched -- pack the unchanged codes with
+ *      qpack_pack_codes;
+ *   bad: optional device int32 (NULL to skip); set to 1 (never cleared) if
+ *      any input is negative or not finite, which is encoded as 0.
+ * Per super-block of 256 weights: step = fp16(fl32(max / L)) and code =
+ * clamp(rint(fl32(v / step)), 0, L), 0 when the step is 0, with L = 255
+ * (Q4K scale and zero codes) or 127 (Q6K scale code) -- the rule of the
+ * nested quantizers, whose own plain stage feeds it. */
+qp_status qpack_encode_nested(const qp_desc* d, const float* s, const float* z,
+                              const qp_weights* out, int32_t* bad, void* stream);
+
 /* Dequantize into W_out (device [N, K] of out_dtype).  QP_F32 gives the fp32
  * evaluation of the format's rule in the order written above (exact for Q6K;
  * the exact value rounded once for AFFINE and SYM4; for Q4K the difference
@@ -219,8 +254,10 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x,
  * shapes whose block count it spreads better over the 256 compute units
  * (N = 14336 at M = 2048: 512 blocks, two full waves, instead of 448, 1.75
  * waves); it reads the activations staged once as fp16 in MFMA fragment
- * order, ceil(M / 16) * 16 * K * 2 bytes.  0 when the call would not use
- * it (another kernel, 256-row tiles, or more than 2^31 staged bytes).  The
+ * order, ceil(M / 16) * 16 * K * 2 bytes, followed by one int32 prescale
+ * exponent per staged row (ceil(M / 16) * 16 * 4 bytes).  0 when the call
+ * would not use it (another kernel, 256-row tiles, or more than 2^31 staged
+ * bytes).  The
  * argument checks of the forward call apply. */
 qp_status qlinear_workspace_bytes(const qp_desc* d, int32_t x_dtype, int64_t M,
                                   int32_t kernel, size_t* bytes);
@@ -245,10 +282,10 @@ qp_status qlinear_forward_ws(const qp_desc* d, const void* x, int32_t x_dtype,
  * capture, serving loops, harnesses that forbid hipMalloc):
  * qlinear_forward_ws without a workspace argument.  Where the call would use
  * a workspace (see qlinear_workspace_bytes) it uses the library's static
- * device scratch instead: 32 MiB per GPU, held from the library's load until
- * the process ends, so ceil(M / 16) * 16 * K <= 16 Mi (e.g. M = 2048 at
- * K = 8192); a larger staging need is QP_EUNSUPPORTED and nothing is
- * enqueued.  Allocates nothing (no hipMalloc, no allocating library call);
+ * device scratch instead: 40 MiB per GPU, held from the library's load until
+ * the process ends, so ceil(M / 16) * 16 * (2 K + 4) bytes <= 40 MiB (e.g.
+ * M = 2048 at K = 8192); a larger staging need is QP_EUNSUPPORTED and
+ * nothing is enqueued.  Allocates nothing (no hipMalloc, no allocating library call);
  * the scratch's device address is looked up once per device on the first
  * call, with that device current.  Every call on a GPU shares that GPU's
  * scratch: calls that overlap on one GPU (other streams, other threads)

@@ -138,12 +138,42 @@ def test_other_entry_points_validate(q):
     assert q.lib.qpack_sizes(ctypes.byref(d), None) == q.QP_EINVAL
 
 
+def test_concat_and_encode_validate(q):
+    """Host-side checks of qpack_concat_n and qpack_encode_nested (no
+    device access: validation fails first)."""
+    w = q._Weights(FAKE, None, FAKE, FAKE, None)
+    parts = [q.QDesc.affine(64, 512), q.QDesc.affine(32, 512)]
+    dins = (q._Desc * 2)(*[p.c() for p in parts])
+    wins = (q._Weights * 2)(w, w)
+    good = q.QDesc.affine(96, 512).c()
+    assert q.lib.qpack_concat_n(ctypes.byref(good), 0, dins, wins, ctypes.byref(w),
+                                None) == q.QP_EINVAL
+    bad_n = q.QDesc.affine(100, 512).c()
+    assert q.lib.qpack_concat_n(ctypes.byref(bad_n), 2, dins, wins, ctypes.byref(w),
+                                None) == q.QP_ESHAPE and "add up" in _err(q)
+    other_k = (q._Desc * 2)(parts[0].c(), q.QDesc.affine(32, 1024).c())
+    assert q.lib.qpack_concat_n(ctypes.byref(good), 2, other_k, wins, ctypes.byref(w),
+                                None) == q.QP_EINVAL and "differs" in _err(q)
+    d4 = q.QDesc.q4k(64, 512).c()
+    w4 = q._Weights(FAKE, None, FAKE, FAKE, FAKE)
+    S = ctypes.c_void_p(FAKE)
+    assert q.lib.qpack_encode_nested(ctypes.byref(d4), S, None, ctypes.byref(w4), None,
+                                     None) == q.QP_EINVAL and "zero points" in _err(q)
+    assert q.lib.qpack_encode_nested(ctypes.byref(q.QDesc.affine(64, 512).c()), S, S,
+                                     ctypes.byref(w4), None, None) == q.QP_EUNSUPPORTED
+    d6 = q.QDesc.q6k(64, 512).c()
+    assert q.lib.qpack_encode_nested(ctypes.byref(d6), S, S, ctypes.byref(w4), None,
+                                     None) == q.QP_EINVAL
+    assert q.lib.qpack_encode_nested(ctypes.byref(d4), ctypes.c_void_p(FAKE + 4), S,
+                                     ctypes.byref(w4), None, None) == q.QP_EALIGN
+
+
 def test_workspace_query_and_checks(q):
     n = ctypes.c_size_t(7)
     d = q.QDesc.affine(64, 512).c()
     # qGEMM: M rounded up to 16 rows of K fp16; other kernels take none
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 300, 2, ctypes.byref(n)) == q.QP_OK
-    assert n.value == 304 * 512 * 2
+    assert n.value == 304 * 512 * 2 + 304 * 4
     # 8192 rows at M = 2048: 256 blocks of 256 rows (one wave) beat 296
     # blocks of 224 rows (two waves): no workspace
     d8 = q.QDesc.affine(8192, 512).c()
@@ -152,7 +182,7 @@ def test_workspace_query_and_checks(q):
     # 14336 rows at M = 2048: 512 blocks of 224 rows beat 448 of 256
     d14 = q.QDesc.affine(14336, 4096).c()
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d14), 1, 2048, 0, ctypes.byref(n)) == q.QP_OK
-    assert n.value == 2048 * 4096 * 2
+    assert n.value == 2048 * 4096 * 2 + 2048 * 4
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 1, 0, ctypes.byref(n)) == q.QP_OK
     assert n.value == 0
     assert q.lib.qlinear_workspace_bytes(ctypes.byref(d), 1, 4, 1, ctypes.byref(n)) == q.QP_OK

@@ -269,7 +269,7 @@ def test_gemm_workspace_tilings_agree(q, N, K, M):
             buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
             xd = to_dev_bits(xb, xdt)
             nb = q.workspace_bytes(d, M, xdt, q.QP_KERNEL_GEMM)
-            assert nb == (M + 15) // 16 * 16 * K * 2
+            assert nb == (M + 15) // 16 * 16 * (K * 2 + 4)   # fragments + exponents
             ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
             y0 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM,
                                    workspace=None)

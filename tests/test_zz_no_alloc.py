@@ -60,7 +60,7 @@ def test_static_other_kernels_and_limit(q):
         assert torch.equal(out, ref)
     big = q.QDesc.affine(14336, 8192, 4, 64, "bf16")
     M = 4096
-    assert q.workspace_bytes(big, M, "bf16", q.QP_KERNEL_AUTO) > 32 << 20
+    assert q.workspace_bytes(big, M, "bf16", q.QP_KERNEL_AUTO) > 40 << 20
     w = q.alloc_weights(big)
     x = torch.zeros((M, big.K), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((M, big.N), dtype=torch.bfloat16, device="cuda")
