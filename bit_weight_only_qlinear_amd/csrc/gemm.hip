@@ -1,69 +1,60 @@
-// qGEMM host side: activation staging (fp16 fragments with the bf16
-// prescale exponents for the 224-row tiles; the exponents alone, into y,
-// for the 256-row tiles), the tiling choice and the dispatch to the
+// qGEMM host side: activation staging (the bf16 prescale exponents and the
+// fp16 fragments, into the workspace, for the 224-row tiles; the exponents
+// alone, into y, for the 256-row tiles), the tiling choice and the dispatch to the
 // per-format kernel instantiations.  The kernels and their design are in
 // gemm_kernels.hpp.
-#include <algorithm>
-
 #include "gemm_kernels.hpp"
 
 namespace qp {
 namespace {
 
-// Stages x [M, K] (bf16 or fp16) for k_gemm224: fp16 in the B-fragment order
-// of v_mfma_f32_16x16x32_f16.  16-byte chunk c = (mb * K/32 + kq) * 64 + l
-// holds row 16 mb + (l & 15), columns 32 kq + 8 (l >> 4) .. + 7 in the order
-// (0,4,1,5,2,6,3,7); rows from M up to the next multiple of 16 are zero.
-// Blocks of 1024 threads: `ks` blocks per 16-row group mb, block q of them
-// converting the q-th of ks equal runs of the group's chunks (1024 is a
-// multiple of 64, so a thread's chunks all belong to one row).  For bf16
-// every block first reduces the rows' max |x| over the whole row, one wave
-// per row reading it contiguously (the group's ks blocks repeat that read,
-// from cache), to the prescale exponent
-// e = 14 - floor(log2 max|x|) (0 for an all-zero row), which scales the
-// row's peak into [2^14, 2^15) -- inside fp16's range; block 0 writes it to
-// xe[row] for the qGEMM's epilogue.
-constexpr int kStageThreads = 1024;
+// Staging for k_gemm224, two kernels.  k_xmax: one wave per activation row
+// reads the row in contiguous 1 KiB pieces and writes its prescale exponent
+// e = 14 - floor(log2 max|x|) (0 for an all-zero row or a padding row),
+// which scales the row's peak into [2^14, 2^15) -- inside fp16's range --
+// to xe[row] (rows up to the next multiple of 16).  k_xprep: x [M, K] (bf16
+// or fp16) as fp16 in the B-fragment order of v_mfma_f32_16x16x32_f16:
+// 16-byte chunk c = (mb * K/32 + kq) * 64 + l holds row 16 mb + (l & 15),
+// columns 32 kq + 8 (l >> 4) .. + 7 in the order (0,4,1,5,2,6,3,7), bf16
+// rows scaled by 2^e; rows from M up to the next multiple of 16 are zero.
+// (One fused kernel, reading each row group twice, was slower: 14.7 vs
+// 5.0 + 6.9 us at M = 2048, K = 4096.)
+__global__ void __launch_bounds__(256) k_xmax(const uint16_t* __restrict__ x, int* __restrict__ xe,
+                                              uint32_t M, uint32_t K, uint32_t Mpad) {
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6), l = threadIdx.x & 63u;
+  if (row >= Mpad) return;   // whole waves: the row is uniform across the wave
+  uint32_t mx = 0;           // |bf16| compares as its bit pattern with the sign cleared
+  if (row < M) {
+    const uint4* xw = reinterpret_cast<const uint4*>(x + (uint64_t)row * K);
+#pragma unroll 8
+    for (uint32_t c = l; c < K / 8u; c += 64u) {
+      const uint4 u = xw[c];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7FFFu, (w[q] >> 16) & 0x7FFFu));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+  const float f = bf16_to_f32(mx);
+  if (l == 0) xe[row] = f == 0.f ? 0 : 14 - ilogbf(f);
+}
 
 template <bool XBF16>
-__global__ void __launch_bounds__(kStageThreads) k_xstage(const uint16_t* __restrict__ x,
-                                                          uint4* __restrict__ xf,
-                                                          int* __restrict__ xe, uint32_t M,
-                                                          uint32_t K, uint32_t ks) {
-  __shared__ uint32_t s_max[16];
-  const uint32_t mb = blockIdx.x / ks, part = blockIdx.x % ks, tid = threadIdx.x;
-  const uint32_t nch = (K / 32u) * 64u;   // chunks of the row group
-  const uint32_t l = tid & 63u, r = l & 15u, row = 16u * mb + r;
-  const uint16_t* xr = x + (uint64_t)row * K + 8u * (l >> 4);
+__global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x, uint4* __restrict__ xf,
+                                               const int* __restrict__ xe, uint32_t M, uint32_t K,
+                                               uint32_t nchunks) {
+  const uint32_t c = blockIdx.x * 256u + threadIdx.x;
+  if (c >= nchunks) return;
+  const uint32_t l = c & 63u, blk = c >> 6, kb = K / 32u;
+  const uint32_t mb = blk / kb, kq = blk - mb * kb;
+  const uint32_t row = 16u * mb + (l & 15u), col = 32u * kq + 8u * (l >> 4);
+  uint4 u = make_uint4(0u, 0u, 0u, 0u);
   int e = 0;
-  if constexpr (XBF16) {
-    // wave w reduces row 16 mb + w, reading it in contiguous 1 KiB pieces
-    const uint32_t wr = tid >> 6, rrow = 16u * mb + wr;
-    uint32_t mx = 0;   // |bf16| compares as its bit pattern with the sign cleared
-    if (rrow < M) {
-      const uint4* xw = reinterpret_cast<const uint4*>(x + (uint64_t)rrow * K);
-      for (uint32_t c = l; c < K / 8u; c += 64u) {
-        const uint4 u = xw[c];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) mx = max(mx, max(w[q] & 0x7FFFu, (w[q] >> 16) & 0x7FFFu));
-      }
-    }
-    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-    if (l == 0) s_max[wr] = mx;
-    __syncthreads();
-    const float f = bf16_to_f32(s_max[r]);
-    e = f == 0.f ? 0 : 14 - ilogbf(f);
-    if (part == 0 && tid < 16) xe[16u * mb + tid] = e;
+  if (row < M) {
+    u = *reinterpret_cast<const uint4*>(x + (uint64_t)row * K + col);
+    if constexpr (XBF16) e = xe[row];
   }
-  // this block's run of chunks (a multiple of 1024 chunks, or the tail)
-  const uint32_t per = ((nch + kStageThreads - 1) / kStageThreads + ks - 1) / ks * kStageThreads;
-  const uint32_t j0 = part * per, j1 = min(nch, j0 + per);
-  for (uint32_t j = j0 + tid; j < j1; j += kStageThreads) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (row < M) u = *reinterpret_cast<const uint4*>(xr + 32u * (j >> 6));
-    xf[(uint64_t)mb * nch + j] = act_chunk<XBF16>(u, e);
-  }
+  xf[c] = act_chunk<XBF16>(u, e);
 }
 
 // Prescale exponent of each bf16 activation row: e = 14 - floor(log2 of the
@@ -152,19 +143,18 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   a.tilesN = (int)cdiv(d.N, n224 ? BN7 : BN);
   if (n224) {   // staging (with the bf16 prescale exponents) into the workspace
     int* xe = const_cast<int*>(a.xe);
-    // enough blocks for the chip: split each 16-row group's conversion over
-    // up to 8 blocks (each repeats the group's max pass, from cache)
-    const int64_t groups = cdiv(M, 16);
-    const uint32_t ks = (uint32_t)std::max<int64_t>(1, std::min<int64_t>(8, 512 / groups));
-    const dim3 grid((unsigned)(groups * ks));
-    if (xdt == BF16)
-      hipLaunchKernelGGL(k_xstage<true>, grid, dim3(kStageThreads), 0, s,
+    const uint32_t mpad = (uint32_t)(cdiv(M, 16) * 16), nch = (uint32_t)(staged_bytes(d, M) / 16u);
+    if (xdt == BF16) {
+      hipLaunchKernelGGL(k_xmax, dim3((mpad + 3) / 4), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), xe, (uint32_t)M, (uint32_t)d.K, mpad);
+      hipLaunchKernelGGL(k_xprep<true>, dim3((nch + 255) / 256), dim3(256), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), xe,
-                         (uint32_t)M, (uint32_t)d.K, ks);
-    else
-      hipLaunchKernelGGL(k_xstage<false>, grid, dim3(kStageThreads), 0, s,
+                         (uint32_t)M, (uint32_t)d.K, nch);
+    } else {
+      hipLaunchKernelGGL(k_xprep<false>, dim3((nch + 255) / 256), dim3(256), 0, s,
                          static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), xe,
-                         (uint32_t)M, (uint32_t)d.K, ks);
+                         (uint32_t)M, (uint32_t)d.K, nch);
+    }
   } else if (xdt == BF16) {   // per-row prescale exponents into y (see k_xexp)
     hipLaunchKernelGGL(k_xexp, dim3((unsigned)M), dim3(256), 0, s, static_cast<const uint16_t*>(x),
                        d.K, y, d.N, ydt, BN, a.tilesN);

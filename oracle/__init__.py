@@ -29,12 +29,20 @@ fp16 conversion keeps subnormals, and the linear layer's result is the fp64
 matmul of the exactly dequantized weights.  Points the pages leave open are
 taken at their plainest reading; each is listed in the module that uses it.
 
+  * The same superscale page, review thread: the original int4 / int6
+    tensors are converted into Q4_K / Q6_K with the codes kept
+    (convert.py: to_q4k, to_q6k).
+
 Parity status per function:
   quantize_* / pack_* / unpack_* / dequant_* / linear : pinned by the tests in
   tests/test_oracle_*.py (closed-form fixtures, lattice exactness, brute-force
   optimal rounding, exhaustive pack round trip, bpw accounting, scalar-loop
-  equality).  snr_db: parity unpinned (the pages' SNR table was measured on
-  GGUF tensors that are not available; only the ordering is checked).
+  equality).  a8w4 (quantize_activations, linear_a8w4): hand-worked tokens
+  and dots, rounding invariants, exact rational brute force.  convert
+  (to_q4k, to_q6k): hand-worked super-blocks, the lossless lattice case,
+  the half-step bound.  snr_db: pinned by hand-worked closed forms; the
+  pages' own SNR figures (GGUF tensors, not available) are not reproduced,
+  only their ordering.
 """
 from .numerics import (bf16_bits_to_f32, f32_to_bf16_bits, f16_bits_to_f32,
                        decode_activations)
