@@ -152,6 +152,35 @@ def gemv_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
     return res
 
 
+def concat_case(q, K, Ns, x_bits, layers, steps, warmup):
+    """Fused-N projections (e.g. q, k, v of one attention layer): the parts
+    as separate forward calls against one forward over their qpack_concat_n
+    stack, `layers` distinct weight sets each, M = 1."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(3)
+    descs = [q.QDesc.affine(n, K, 4, 64, "bf16") for n in Ns]
+    xd = torch.from_numpy(np.ascontiguousarray(x_bits[:1]).view(np.int16)).view(torch.bfloat16).cuda()
+    parts, fused, ys, yf = [], [], [], []
+    for _ in range(layers):
+        bufs = [q.qpack_quantize(d, torch.from_numpy(rng.normal(0, 0.02, size=(d.N, K)).astype(np.float32)).cuda())
+                for d in descs]
+        dout, out = q.concat_n(descs, bufs)
+        parts.append(bufs)
+        fused.append(out)
+        ys.append([torch.empty((1, d.N), dtype=torch.bfloat16, device="cuda") for d in descs])
+        yf.append(torch.empty((1, dout.N), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    sep = [(lambda d=d, w=w, y=y: q.qlinear_forward(d, xd, w, out=y))
+           for bl, yl in zip(parts, ys) for d, w, y in zip(descs, bl, yl)]
+    one = [(lambda w=w, y=y: q.qlinear_forward(dout, xd, w, out=y)) for w, y in zip(fused, yf)]
+    _, ms_sep = time_graph(sep, steps, warmup)
+    _, ms_one = time_graph(one, steps, warmup)
+    del parts, fused
+    torch.cuda.empty_cache()
+    return dict(us_separate=ms_sep * 1e3 / (steps * layers), us_fused=ms_one * 1e3 / (steps * layers))
+
+
 def a8w4_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
     """The a8w4 layer: per-token int8 quantization of x, then the int8 MFMA
     forward, per layer (both kernels timed)."""
@@ -312,6 +341,8 @@ def main():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--quick", action="store_true", help="headline case only")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--qgemm-only", action="store_true",
+                    help="only the prefill qGEMM case (for profiling); prints its own line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -337,6 +368,15 @@ def main():
         torch.cuda.synchronize()
         log("copy calibration: 1 GiB read + 1 GiB written")
         del a, b
+
+    if args.qgemm_only:
+        w5 = synth.make("prefill_affine", seed=0)
+        r = gemm_case(q, q.QDesc.affine(14336, 4096, 4, 64, "bf16"), w5.W, w5.x_bits,
+                      max(10, args.steps // 10), max(3, args.warmup // 4))
+        print(json.dumps({"qgemm_only": True, "us_per_call": round(r["us_per_call"], 2),
+                          "tflops": round(r["tflops"], 2), "frac": round(r["frac"], 4)}),
+              flush=True)
+        return
 
     # ---- headline: decode qGEMV int4 affine
     log("generating decode_affine weights")
@@ -389,6 +429,15 @@ def main():
                                us_per_call=round(r["us_per_call"], 3)))
             log(extras[-1])
         del w4, w4s
+        xq = synth.make("decode_affine", seed=1, N=8).x_bits   # x ~ N(0, 1) bf16, K = 4096
+        r = concat_case(q, 4096, (4096, 1024, 1024), xq, 32, max(20, args.steps // 4),
+                        args.warmup)
+        extras.append(dict(workload="fused-N projections (q 4096 + k 1024 + v 1024 rows, "
+                                    "K=4096, int4 affine gs64, M=1): three forward calls vs one "
+                                    "over their qpack_concat_n stack",
+                           us_separate=round(r["us_separate"], 3),
+                           us_fused=round(r["us_fused"], 3)))
+        log(extras[-1])
         log("generating prefill_affine weights")
         w5 = synth.make("prefill_affine", seed=0)
         r = gemm_case(q, q.QDesc.affine(14336, 4096, 4, 64, "bf16"), w5.W, w5.x_bits,

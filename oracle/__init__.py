@@ -32,6 +32,8 @@ taken at their plainest reading; each is listed in the module that uses it.
   * The same superscale page, review thread: the original int4 / int6
     tensors are converted into Q4_K / Q6_K with the codes kept
     (convert.py: to_q4k, to_q6k).
+  * The same page, "Ablation study": alternative scale / zero encodings
+    (ablation.py: encode_value, dequant_f64, bits_per_weight).
 
 Parity status per function:
   quantize_* / pack_* / unpack_* / dequant_* / linear : pinned by the tests in
@@ -40,7 +42,9 @@ Parity status per function:
   equality).  a8w4 (quantize_activations, linear_a8w4): hand-worked tokens
   and dots, rounding invariants, exact rational brute force.  convert
   (to_q4k, to_q6k): hand-worked super-blocks, the lossless lattice case,
-  the half-step bound.  snr_db: pinned by hand-worked closed forms; the
+  the half-step bound.  ablation: the table's bpw column, the uint8 case
+  against the pinned conversion, hand-worked lattice and rounding cases;
+  its SNR values are parity unpinned (GGUF tensors), only the orderings.  snr_db: pinned by hand-worked closed forms; the
   pages' own SNR figures (GGUF tensors, not available) are not reproduced,
   only their ordering.
 """
