@@ -8,17 +8,19 @@
 namespace qp {
 namespace {
 
-// Staging for k_gemm224, two kernels.  k_xmax: one wave per activation row
-// reads the row in contiguous 1 KiB pieces and writes its prescale exponent
+// Staging for k_gemm224.  Every bf16 row gets a prescale exponent
 // e = 14 - floor(log2 max|x|) (0 for an all-zero row or a padding row),
 // which scales the row's peak into [2^14, 2^15) -- inside fp16's range --
-// to xe[row] (rows up to the next multiple of 16).  k_xprep: x [M, K] (bf16
-// or fp16) as fp16 in the B-fragment order of v_mfma_f32_16x16x32_f16:
-// 16-byte chunk c = (mb * K/32 + kq) * 64 + l holds row 16 mb + (l & 15),
-// columns 32 kq + 8 (l >> 4) .. + 7 in the order (0,4,1,5,2,6,3,7), bf16
-// rows scaled by 2^e; rows from M up to the next multiple of 16 are zero.
-// (One fused kernel, reading each row group twice, was slower: 14.7 vs
-// 5.0 + 6.9 us at M = 2048, K = 4096.)
+// stored in xe[row] (rows up to the next multiple of 16), and x [M, K]
+// (bf16 or fp16) goes to fp16 in the B-fragment order of
+// v_mfma_f32_16x16x32_f16: 16-byte chunk c = (mb * K/32 + kq) * 64 + l
+// holds row 16 mb + (l & 15), columns 32 kq + 8 (l >> 4) .. + 7 in the
+// order (0,4,1,5,2,6,3,7), bf16 rows scaled by 2^e; rows from M up to the
+// next multiple of 16 are zero.  k_xmax (one wave per row: the exponent)
+// then k_xprep (the conversion) for any K; k_xstage and k_xstage8 do both
+// in one pass over x where a wave can hold a whole row (at M = 2048,
+// K = 4096: 8.96 us, against 10.46 for k_xstage and 4.8 + 6.7 for the two
+// passes; a block that read each 16-row group twice took 14.7).
 __global__ void __launch_bounds__(256) k_xmax(const uint16_t* __restrict__ x, int* __restrict__ xe,
                                               uint32_t M, uint32_t K, uint32_t Mpad) {
   const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6), l = threadIdx.x & 63u;
@@ -55,6 +57,101 @@ __global__ void __launch_bounds__(256) k_xprep(const uint16_t* __restrict__ x, u
     if constexpr (XBF16) e = xe[row];
   }
   xf[c] = act_chunk<XBF16>(u, e);
+}
+
+// The two kernels above in one pass, for rows of up to NU * 512 columns:
+// one wave per staged row holds the whole row in registers (NU 16-byte
+// chunks per lane), takes its maximum, writes the exponent, converts and
+// stores every chunk at its fragment position.  x is read once.  A 128-byte
+// line of the fragments is written by 8 waves (rows), 16 bytes each, and
+// completed in the L2.
+template <bool XBF16, int NU>
+__global__ void __launch_bounds__(256) k_xstage(const uint16_t* __restrict__ x, uint4* __restrict__ xf,
+                                                int* __restrict__ xe, uint32_t M, uint32_t K,
+                                                uint32_t Mpad) {
+  const uint32_t row = blockIdx.x * 4u + (threadIdx.x >> 6), l = threadIdx.x & 63u;
+  if (row >= Mpad) return;   // whole waves: the row is uniform across the wave
+  const uint32_t nq = K / 8u;   // 8-column chunks per row
+  uint4 u[NU];
+  uint32_t mx = 0;
+  const uint4* xw = reinterpret_cast<const uint4*>(x + (uint64_t)row * K);
+#pragma unroll
+  for (int t = 0; t < NU; ++t) {
+    const uint32_t q = l + 64u * t;
+    u[t] = row < M && q < nq ? xw[q] : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (XBF16) {
+      const uint32_t w[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mx = max(mx, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+    }
+  }
+  int e = 0;
+  if constexpr (XBF16) {
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    const float f = bf16_to_f32(mx);
+    e = f == 0.f ? 0 : 14 - ilogbf(f);
+    if (l == 0) xe[row] = e;
+  }
+  // chunk q of the row: fragment (row / 16, q / 4), lane (row % 16) + 16 (q % 4)
+  const uint32_t base = (row / 16u) * (K / 32u) * 64u + (row % 16u);
+#pragma unroll
+  for (int t = 0; t < NU; ++t) {
+    const uint32_t q = l + 64u * t;
+    if (q < nq) xf[base + (q / 4u) * 64u + 16u * (q % 4u)] = act_chunk<XBF16>(u[t], e);
+  }
+}
+
+// The same with 8 rows per block (K <= 4096): each wave converts its row as
+// above, the block transposes the chunks through LDS, and every store
+// instruction writes whole 128-byte lines (8 rows' chunks of one fragment
+// column group).  LDS holds line L (fragment column group) position p at
+// (8 L + p) * 16 with p = row ^ (L & 7), so that the 8 lanes of a write
+// phase hit 8 different bank groups.
+template <bool XBF16, int NU>
+__global__ void __launch_bounds__(512) k_xstage8(const uint16_t* __restrict__ x, uint4* __restrict__ xf,
+                                                 int* __restrict__ xe, uint32_t M, uint32_t K) {
+  extern __shared__ __attribute__((aligned(16))) uint4 sx[];   // K / 8 lines' worth: K chunks
+  const uint32_t w = threadIdx.x >> 6, l = threadIdx.x & 63u;
+  const uint32_t row = blockIdx.x * 8u + w;
+  const uint32_t nq = K / 8u;
+  uint4 u[NU];
+  uint32_t mx = 0;
+  const uint4* xw = reinterpret_cast<const uint4*>(x + (uint64_t)row * K);
+#pragma unroll
+  for (int t = 0; t < NU; ++t) {
+    const uint32_t q = l + 64u * t;
+    u[t] = row < M && q < nq ? xw[q] : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (XBF16) {
+      const uint32_t v[4] = {u[t].x, u[t].y, u[t].z, u[t].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mx = max(mx, max(v[k] & 0x7FFFu, (v[k] >> 16) & 0x7FFFu));
+    }
+  }
+  int e = 0;
+  if constexpr (XBF16) {
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    const float f = bf16_to_f32(mx);
+    e = f == 0.f ? 0 : 14 - ilogbf(f);
+    if (l == 0) xe[row] = e;
+  }
+  // chunk q of this row belongs to line q (fragment q / 4, lanes 16 (q % 4) + ...)
+#pragma unroll
+  for (int t = 0; t < NU; ++t) {
+    const uint32_t q = l + 64u * t;
+    if (q < nq) sx[8u * q + (w ^ (q & 7u))] = act_chunk<XBF16>(u[t], e);
+  }
+  __syncthreads();
+  // line L of the block: fragment L / 4, lanes 16 (L % 4) + r0 .. + 7
+  const uint32_t r0 = (blockIdx.x * 8u) % 16u;
+  const uint32_t base = (blockIdx.x * 8u / 16u) * (K / 32u) * 64u + r0;
+#pragma unroll
+  for (int t = 0; t < NU; ++t) {
+    const uint32_t i = threadIdx.x + 512u * t;   // i < K: line i / 8, position i % 8
+    if (i < K) {
+      const uint32_t L = i / 8u, p = i % 8u;
+      xf[base + (L / 4u) * 64u + 16u * (L % 4u) + (p ^ (L & 7u))] = sx[i];
+    }
+  }
 }
 
 // Prescale exponent of each bf16 activation row: e = 14 - floor(log2 of the
@@ -144,7 +241,21 @@ hipError_t launch_gemm(const Desc& d, const void* x, int xdt, int64_t M, const B
   if (n224) {   // staging (with the bf16 prescale exponents) into the workspace
     int* xe = const_cast<int*>(a.xe);
     const uint32_t mpad = (uint32_t)(cdiv(M, 16) * 16), nch = (uint32_t)(staged_bytes(d, M) / 16u);
-    if (xdt == BF16) {
+    // bf16: one pass over x (8 rows per block up to K = 4096, one wave per
+    // row up to 8192), else the exponent pass and the conversion pass
+    const int64_t nu = cdiv(d.K, 512);   // 16-byte chunks per lane for one wave per row
+    if (xdt == BF16 && d.K <= 4096) {
+      auto fn = nu <= 1 ? k_xstage8<true, 1> : nu <= 2 ? k_xstage8<true, 2> : nu <= 4 ? k_xstage8<true, 4>
+              : k_xstage8<true, 8>;
+      hipLaunchKernelGGL(fn, dim3(mpad / 8), dim3(512), (unsigned)(d.K * 16), s,
+                         static_cast<const uint16_t*>(x), static_cast<uint4*>(ws), xe, (uint32_t)M,
+                         (uint32_t)d.K);
+    } else if (xdt == BF16 && nu <= 16) {
+      auto fn = nu <= 1 ? k_xstage<true, 1> : nu <= 2 ? k_xstage<true, 2> : nu <= 4 ? k_xstage<true, 4>
+              : nu <= 8 ? k_xstage<true, 8> : k_xstage<true, 16>;
+      hipLaunchKernelGGL(fn, dim3((mpad + 3) / 4), dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                         static_cast<uint4*>(ws), xe, (uint32_t)M, (uint32_t)d.K, mpad);
+    } else if (xdt == BF16) {
       hipLaunchKernelGGL(k_xmax, dim3((mpad + 3) / 4), dim3(256), 0, s,
                          static_cast<const uint16_t*>(x), xe, (uint32_t)M, (uint32_t)d.K, mpad);
       hipLaunchKernelGGL(k_xprep<true>, dim3((nch + 255) / 256), dim3(256), 0, s,

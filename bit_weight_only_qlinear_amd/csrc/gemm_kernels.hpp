@@ -65,7 +65,7 @@ struct GemmArgs {
   const void* zeros;
   const void* steps;
   const void* x;
-  const void* xf;   // activations staged by k_xprep (k_gemm224), else null
+  const void* xf;   // activations staged for k_gemm224 (gemm.hip), else null
   const int* xe;    // their prescale exponents (bf16, k_gemm224), else null
   const void* bias;
   void* y;
@@ -623,7 +623,7 @@ k_gemm(GemmArgs a) {
 // 7/8 the work each.  A wave then owns 112 weight rows, not a multiple of
 // 32, so this kernel runs v_mfma_f32_16x16x32_f16: 7 x 4 tiles of 16 x 16
 // per wave (wave grid 2 (n) x 4 (m) as in k_gemm).  The activations are
-// staged once per call by k_xprep as fp16 in that MFMA's B-fragment order,
+// staged once per call (gemm.hip) as fp16 in that MFMA's B-fragment order,
 // and each wave loads its B fragments straight into registers, one step
 // ahead; only the weight tile goes through LDS, staged, swizzled and
 // dequantized as in k_gemm (rows 224..255 of the LDS tile are unused).
