@@ -347,6 +347,17 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
   float4_t D[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float4_t DX = {0.f, 0.f, 0.f, 0.f};
 
+  // Formats whose offset T = -S (MAG + c) has a constant c (Q6K: 32,
+  // grouped SYM4: 8) subtract (MAG + c) sum x inside the accumulator with one
+  // more MFMA against B = -(MAG + c) (exact in bf16 and fp16), so the group
+  // sum is sum q x and the epilogue is one FMA per value: VALU work per
+  // group traded for MFMA work, which has room.
+  constexpr bool COFF = KIND == S_Q6K || (KIND == S_SYM4 && GS > 0);
+  const uint32_t coff = XBF16 ? f32_to_bf16_rne(-(MAG + (KIND == S_Q6K ? 32.f : 8.f)))
+                              : f32_to_f16_rne(-(MAG + (KIND == S_Q6K ? 32.f : 8.f)));
+  const uint4 BC = make_uint4(coff | (coff << 16), coff | (coff << 16), coff | (coff << 16),
+                              coff | (coff << 16));
+
   // group gg of the block is complete in Dd, DXd: apply its (S, T)
   auto epilogue = [&](const SxStage<KIND, GS>& s, int gg, const float4_t (&Dd)[2],
                       const float4_t& DXd) __attribute__((always_inline)) {
@@ -355,7 +366,8 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
       float S, T;
       group_st<KIND, GS, MBF16>(s, i, gg, MAG, S, T);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[i][v] = fmaf(T, DXd[v], fmaf(S, Dd[i][v], acc[i][v]));
+      for (int v = 0; v < 4; ++v)
+        acc[i][v] = COFF ? fmaf(S, Dd[i][v], acc[i][v]) : fmaf(T, DXd[v], fmaf(S, Dd[i][v], acc[i][v]));
     }
   };
 
@@ -403,19 +415,21 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
         for (int i = 0; i < 2; ++i) {
           const uint4 Bq = code_frag<KIND, XBF16>(W[i][t], 0u, H[i][t]);
           D[i] = mfma<XBF16>(Al, Bq, D[i]);
+          D[i] = mfma<XBF16>(Al, BC, D[i]);
           Dh[i] = mfma<XBF16>(Ah, Bq, Dh[i]);
+          Dh[i] = mfma<XBF16>(Ah, BC, Dh[i]);
         }
-        DX = mfma<XBF16>(Al, ONES, DX);
-        const float4_t DXh = mfma<XBF16>(Ah, ONES, float4_t{0.f, 0.f, 0.f, 0.f});
         epilogue(s, 2 * t, D, DX);
-        epilogue(s, 2 * t + 1, Dh, DXh);
-        D[0] = D[1] = DX = float4_t{0.f, 0.f, 0.f, 0.f};
+        epilogue(s, 2 * t + 1, Dh, DX);
+        D[0] = D[1] = float4_t{0.f, 0.f, 0.f, 0.f};
       } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
           D[i] = mfma<XBF16>(A, code_frag<KIND, XBF16>(W[i][t], KIND == S_AFF8 ? W2[i][t] : 0u, 0u),
                              D[i]);
-        DX = mfma<XBF16>(A, ONES, DX);
+          if constexpr (COFF) D[i] = mfma<XBF16>(A, BC, D[i]);
+        }
+        if constexpr (!COFF) DX = mfma<XBF16>(A, ONES, DX);
         if constexpr (!PERCH) {
           // a group ends every GS / 32 steps
           constexpr int spg = (GS > 0 ? GS : 128) / 32;
