@@ -54,6 +54,42 @@ __device__ __forceinline__ float dpp_f(float old, float v) {
                                          ROW_MASK, BANK_MASK, BOUND));
 }
 
+#define QP_DPP_ROW_HALF_MIRROR 0x141
+
+// Wave sums of R <= 8 per-lane values at once (a transposed reduction):
+// permlane32 / permlane16 swaps pair the values up across lane halves, an
+// xor-8 exchange and three DPP steps finish inside 8-lane groups.
+// Afterwards the total of value v is in all 8 lanes of group (R, h),
+// R = lane >> 4, h = (lane >> 3) & 1, where v = 4 h + ((R & 1) << 1 | R >> 1).
+template <int R>
+__device__ __forceinline__ float wave_sums8(const float (&v)[R], int lane) {
+  static_assert(R >= 1 && R <= 8, "up to 8 values");
+  float b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (2 * k >= R) { b[k] = 0.f; continue; }
+    const float hi = 2 * k + 1 < R ? v[2 * k + 1] : 0.f;
+    // lanes 0-31: value 2k over lanes (l, l + 32); lanes 32-63: value 2k + 1
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * k]), __float_as_uint(hi),
+                                                    false, false);
+    b[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  float c[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    // 16-lane rows 0..3: values 4k, 4k + 2, 4k + 1, 4k + 3 over 4 lanes each
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(b[2 * k]),
+                                                    __float_as_uint(b[2 * k + 1]), false, false);
+    c[k] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool h = (lane & 8) != 0;
+  float d = (h ? c[1] : c[0]) + dpp_f<QP_DPP_ROW_ROR8>(0.f, h ? c[0] : c[1]);
+  d += dpp_f<QP_DPP_QUAD_1032>(0.f, d);
+  d += dpp_f<QP_DPP_QUAD_2301>(0.f, d);
+  d += dpp_f<QP_DPP_ROW_HALF_MIRROR>(0.f, d);
+  return d;
+}
+
 // Sum over the 16 lanes of each DPP row; every lane of the row gets it.
 __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<QP_DPP_QUAD_1032>(0.f, v);
