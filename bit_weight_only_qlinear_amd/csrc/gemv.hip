@@ -223,14 +223,14 @@ struct Batch {
 template <int KIND, int RB, int CPL, int RLO = 0, int RHI = RB>
 __device__ __forceinline__ void load_batch(const GemvArgs& a, __amdgpu_buffer_rsrc_t rqw,
                                            __amdgpu_buffer_rsrc_t rqh, const uint32_t (&lane_cw)[CPL],
-                                           Batch<KIND, RB, CPL>& B, int64_t r, int64_t rowEnd) {
+                                           Batch<KIND, RB, CPL>& B, int r, int rowEnd) {
   const uint32_t C = (uint32_t)a.C;
 #pragma unroll
   for (int rb = RLO; rb < RHI; ++rb) {
     // rows past the end of a partial batch re-read the last valid row
     // (already on its way to this wave's caches); their results are never
     // stored
-    const uint32_t n = (uint32_t)max(min(r + rb, rowEnd - 1), (int64_t)0);
+    const uint32_t n = (uint32_t)max(min(r + rb, rowEnd - 1), 0);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       B.cw[rb][j] = __builtin_bit_cast(
@@ -379,8 +379,8 @@ __device__ __forceinline__ void compute_batch(const GemvArgs& a, const uint8_t* 
                                               const Batch<KIND, RB, CPL>& B,
                                               const uint32_t (&lane_meta)[CPL][GP],
                                               const uint32_t (&lane_step)[CPL],
-                                              const uint32_t (&row_base)[kMeta], int64_t lrow0,
-                                              int64_t lrmax,
+                                              const uint32_t (&row_base)[kMeta], int lrow0,
+                                              int lrmax,
                                               const uint32_t (&xq)[CPL][MT][XW],
                                               const float (&xs)[CPL][MT][GP],
                                               float (&yacc)[RB][MT]) {
@@ -486,11 +486,13 @@ k_gemv(GemvArgs a) {
   const int kw = wave % KW;
   const int team = wave / KW;
   const int RW = 4 / KW;
-  const int64_t brow0 = (int64_t)blockIdx.x * RW * a.RPT;   // first row of the block
-  const int64_t row0 = brow0 + (int64_t)team * a.RPT;
-  const int64_t rowEnd = min(row0 + a.RPT, a.N);
-  const int64_t rowStop = row0 + a.RPT;   // same trip count for every team
-  const int64_t brows = min((int64_t)RW * a.RPT, a.N - brow0);
+  // row indices fit 32 bits: every buffer is < 2 GiB (host check)
+  const int NR = (int)a.N;
+  const int brow0 = (int)blockIdx.x * RW * a.RPT;   // first row of the block
+  const int row0 = brow0 + team * a.RPT;
+  const int rowEnd = min(row0 + a.RPT, NR);
+  const int rowStop = row0 + a.RPT;   // same trip count for every team
+  const int brows = min(RW * a.RPT, NR - brow0);
   const int mbase = blockIdx.y * MT;
   const int C = a.C;
   const int cbase = kw * CPL * 64;
@@ -640,7 +642,7 @@ k_gemv(GemvArgs a) {
     }
   }
 
-  auto finish = [&](float (&yacc)[RB][MT], int64_t r) {
+  auto finish = [&](float (&yacc)[RB][MT], int r) {
     if constexpr (MT == 1 && multi_sum(KIND)) {
       if (KW == 1) {
         // all rows of the batch at once; 8 lanes store in parallel
@@ -650,7 +652,7 @@ k_gemv(GemvArgs a) {
         const float t = wave_sums8<RB>(v, lane);
         const int R = lane >> 4;
         const int rb = 4 * ((lane >> 3) & 1) + (((R & 1) << 1) | (R >> 1));
-        const int64_t n = r + rb;
+        const int n = r + rb;
         if ((lane & 7) == 0 && rb < RB && n < rowEnd && mbase < a.M) {
           const float bv =
               a.meta_row[3] ? xval<XBF16>(lds_read<uint16_t>(smem, row_base[3] + 2u * (uint32_t)(n - brow0)))
@@ -668,7 +670,7 @@ k_gemv(GemvArgs a) {
       if (lane == 63) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          const int64_t n = r + rb;
+          const int n = r + rb;
           if (n < rowEnd) {
             const float bv =
                 a.meta_row[3] ? xval<XBF16>(lds_read<uint16_t>(smem, row_base[3] + 2u * (uint32_t)(n - brow0)))
@@ -692,7 +694,7 @@ k_gemv(GemvArgs a) {
         const int rb = lane / MT, m = lane % MT;
         float v = 0.f;
         for (int q = 0; q < KW; ++q) v += red[wave + q][rb][m];
-        const int64_t n = r + rb;
+        const int n = r + rb;
         if (n < rowEnd && mbase + m < a.M) {
           const float bv =
               a.meta_row[3] ? xval<XBF16>(lds_read<uint16_t>(smem, row_base[3] + 2u * (uint32_t)(n - brow0)))
@@ -707,7 +709,7 @@ k_gemv(GemvArgs a) {
   float yacc[RB][MT];
   if constexpr (NB == 1) {
     // ---- one batch in flight at a time (normally a wave owns one batch)
-    for (int64_t r = row0; r < rowStop; r += RB) {
+    for (int r = row0; r < rowStop; r += RB) {
       if (KW == 1 && r >= rowEnd) break;
       if (r != row0 && r < rowEnd) load_batch<KIND, RB, CPL>(a, rqw, rqh, lane_cw, B0, r, rowEnd);
       compute_batch<KIND, XBF16, MT, CPL, RB, XW, GP>(a, smem, B0, lane_meta, lane_step, row_base,
@@ -719,7 +721,7 @@ k_gemv(GemvArgs a) {
   // ---- row loop, double-buffered: the next batch's loads are in flight
   // while the current one is computed
   Batch<KIND, RB, CPL> B1;
-  for (int64_t r = row0; r < rowStop; r += 2 * RB) {
+  for (int r = row0; r < rowStop; r += 2 * RB) {
     if (KW == 1 && r >= rowEnd) break;
     if (r + RB < rowEnd) load_batch<KIND, RB, CPL>(a, rqw, rqh, lane_cw, B1, r + RB, rowEnd);
     compute_batch<KIND, XBF16, MT, CPL, RB, XW, GP>(a, smem, B0, lane_meta, lane_step, row_base,
