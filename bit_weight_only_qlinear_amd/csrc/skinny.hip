@@ -179,19 +179,25 @@ __device__ __forceinline__ void meta_ld(const SxArgs& a, const unsigned char* ld
   }
 }
 
-template <int KIND, int GS, bool LDSM>
+// PART: 3 = everything; 1 = the global loads only (codes, activations, and
+// metadata when it is not staged); 2 = the staged metadata only (LDS reads).
+template <int KIND, int GS, bool LDSM, int PART = 3>
 __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* lds, int kb, int lane,
                                         int64_t n0, int64_t mrow, SxStage<KIND, GS>& s) {
   const uint32_t c0 = (uint32_t)kb * kSxCols;
   const int g = lane >> 4, r16 = lane & 15;
+  constexpr bool GLOB = (PART & 1) != 0;
+  constexpr bool META = LDSM ? (PART & 2) != 0 : GLOB;
   const uint32_t K = (uint32_t)a.K;
   // activations of row mrow: step t takes columns c0 + 32 t + 8 g .. + 8
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.x, a.x_bytes);
   const uint32_t xo = mrow < a.M ? (uint32_t)mrow * K * 2u + 2u * (c0 + 8u * g) : kOOB;
+  if constexpr (GLOB) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    s.x[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rx, xo == kOOB ? kOOB : xo + 64u * t, 0, 0));
+    for (int t = 0; t < 4; ++t)
+      s.x[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rx, xo == kOOB ? kOOB : xo + 64u * t, 0, 0));
+  }
   constexpr uint32_t B = code_bits(KIND);
   const __amdgpu_buffer_rsrc_t rq = rsrc(a.qw, a.qw_bytes);
   const __amdgpu_buffer_rsrc_t r0 = rsrc(a.meta[0], a.meta_bytes[0]);
@@ -203,7 +209,8 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* ld
     const int64_t n = n0 + 16 * i + r16;
     const bool ok = n < a.N;
     const uint32_t off = ok ? (uint32_t)n * (K * B / 8u) + (c0 + 32u * g) * B / 8u : kOOB;
-    if constexpr (B == 2) {
+    if constexpr (!GLOB) {
+    } else if constexpr (B == 2) {
       const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 2));
       s.w[i][0] = v.x; s.w[i][1] = v.y;
     } else {
@@ -214,7 +221,7 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* ld
         s.w[i][4 * c] = v.x; s.w[i][4 * c + 1] = v.y; s.w[i][4 * c + 2] = v.z; s.w[i][4 * c + 3] = v.w;
       }
     }
-    if constexpr (KIND == S_Q6K) {
+    if constexpr (KIND == S_Q6K && GLOB) {
       const __amdgpu_buffer_rsrc_t rh = rsrc(a.qh, a.qh_bytes);
       const uint32_t ho = ok ? (uint32_t)n * (K / 4u) + (c0 + 32u * g) / 4u : kOOB;
       const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rh, ho, 0, 2));
@@ -222,7 +229,8 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* ld
     }
     // metadata of row n for the block's groups (rows past N read 0)
     const uint32_t rl = (uint32_t)(16 * i + r16), rg = (uint32_t)n;
-    if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
+    if constexpr (!META) {
+    } else if constexpr (KIND == S_AFF2 || KIND == S_AFF4 || KIND == S_AFF8) {
       // 128 / GS groups of 2 bytes: scales into m[0..1], biases into m[2..3]
       constexpr int MB = 256 / GS;
       s.m[i][1] = s.m[i][3] = 0;
@@ -442,20 +450,21 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
     });
   };
 
+  // The block's metadata slabs (rows n0 .. n0 + 31, contiguous in each
+  // array; rows past N read 0) go into LDS with direct buffer->LDS loads
+  // (1 KiB per wave instruction, regions padded to whole KiB), issued before
+  // the first code loads so that waiting for them does not wait for those.
   if constexpr (LDSM) {
-    // the block's metadata slabs (rows n0 .. n0 + 31, contiguous in each
-    // array; rows past N read 0) into LDS, 16 bytes per thread and load
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
-      const uint32_t nb = 32u * a.meta_row[q];   // a multiple of 16
-      if (nb == 0) continue;
+      const uint32_t pieces = (32u * a.meta_row[q] + 1023u) / 1024u;
       const __amdgpu_buffer_rsrc_t r = rsrc(a.meta[q], a.meta_bytes[q]);
       const uint32_t base = (uint32_t)n0 * a.meta_row[q];
-      for (uint32_t j = 16u * (uint32_t)tid; j < nb; j += 16u * 64u * kSxWaves)
-        *reinterpret_cast<uint4*>(s_meta + a.meta_lds[q] + j) =
-            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, base + j, 0, 0));
+      for (uint32_t pc = (uint32_t)wave; pc < pieces; pc += kSxWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(s_meta + a.meta_lds[q] + 1024u * pc), 16,
+            base + 1024u * pc + 16u * (uint32_t)lane, 0, 0, 0);
     }
-    __syncthreads();
   }
 
   // the wave's column blocks: wave, wave + 8, ...; kSxStages - 1 ahead
@@ -463,8 +472,28 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
   const int J = wave < KB ? (KB - wave + kSxWaves - 1) / kSxWaves : 0;
   sfor<kSxStages - 1>([&](auto P) {
     constexpr int p = decltype(P)::value;
-    if (p < J) sx_load<KIND, GS, LDSM>(a, s_meta, wave + p * kSxWaves, lane, n0, mrow, st[p]);
+    if (p < J) sx_load<KIND, GS, LDSM, 1>(a, s_meta, wave + p * kSxWaves, lane, n0, mrow, st[p]);
   });
+
+  if constexpr (LDSM) {
+    // the slab copies are older than the code loads: wait for them only
+    // (all loads where this wave has fewer blocks than stages ahead)
+    constexpr int B = code_bits(KIND);
+    constexpr int n = (kSxStages - 1) * (4 + 2 * (B == 2 ? 1 : B / 4) + (KIND == S_Q6K ? 2 : 0));
+    static_assert(n < 64, "vmcnt range");
+    if (J >= kSxStages - 1)
+      __builtin_amdgcn_s_waitcnt((n & 0xF) | (0x7 << 4) | (0xF << 8) | ((n >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+    __syncthreads();
+  }
+
+  if constexpr (LDSM) {
+    sfor<kSxStages - 1>([&](auto P) {
+      constexpr int p = decltype(P)::value;
+      if (p < J) sx_load<KIND, GS, LDSM, 2>(a, s_meta, wave + p * kSxWaves, lane, n0, mrow, st[p]);
+    });
+  }
   for (int j0 = 0; j0 < J; j0 += kSxStages) {
     sfor<kSxStages>([&](auto Q) {
       constexpr int q = decltype(Q)::value;
@@ -558,7 +587,7 @@ hipError_t launch_skinny(const Desc& d, const void* x, int xdt, int64_t M, const
     a.meta_row[q] = (uint32_t)(bytes[2 + q] / (size_t)d.N);
     if (d.fmt == SYM4 && d.gs == d.K && q == 0) a.meta_row[q] = 0;   // scale applied at the end
     a.meta_lds[q] = lds;
-    lds += 32u * a.meta_row[q];
+    lds += (32u * a.meta_row[q] + 1023u) & ~1023u;   // whole KiB: the copies' unit
   }
   const bool lm = lds > 0 && lds <= kSxMetaLds;
   if (!lm) lds = 0;
