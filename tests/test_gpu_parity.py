@@ -256,7 +256,7 @@ def test_gemm_forward(q, N, K, M):
 
 
 @pytest.mark.parametrize("N,K,M", [(130, 512, 1), (257, 1280, 33), (520, 768, 300),
-                                   (64, 4096, 257)])
+                                   (64, 4096, 257), (130, 5120, 17), (40, 8192, 40)])
 def test_gemm_workspace_tilings_agree(q, N, K, M):
     """224-row tiles (staged activations) and 256-row tiles: same fp16
     operands, fp32 sums in another order; a workspace full of NaN bytes
@@ -284,6 +284,32 @@ def test_gemm_workspace_tilings_agree(q, N, K, M):
             xf = xd.float()
             bound = K * 2.0 ** -23 * (xf.abs() @ wd.abs().T) + 1e-30
             assert ((y0 - y1).abs() <= bound).all()
+
+
+def test_gemm_workspace_long_rows(q):
+    """Per-channel SYM4 past K = 8192, where the activations are staged by
+    the exponent pass and the conversion pass (rows too long to hold in one
+    wave's registers): a workspace full of NaN bytes, both tilings."""
+    N, K, M = 72, 16384, 33
+    d = q.QDesc.sym4(N, K)
+    W = _weights(N, K, 3)
+    xb = synth.draw_activations(np.random.default_rng(9), M, K, "bf16")
+    buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
+    xd = to_dev_bits(xb, "bf16")
+    nb = q.workspace_bytes(d, M, "bf16", q.QP_KERNEL_GEMM)
+    assert nb == (M + 15) // 16 * 16 * (K * 2 + 4)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    y1 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM, workspace=ws)
+    y0 = q.qlinear_forward(d, xd, buf, y_dtype="f32", kernel=q.QP_KERNEL_GEMM, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y1).all()
+    f = qformat_of(d)
+    qz = oracle.quantize(W, f)
+    w64 = oracle.dequant_f64(qz, f)
+    x64 = oracle.decode_activations(xb, "bf16")
+    y_ref = oracle.linear_f64(x64, qz, f, w64=w64)
+    check_linear(y1, y_ref, x64, np.abs(w64).max(), K, "f32")
+    check_linear(y0, y_ref, x64, np.abs(w64).max(), K, "f32")
 
 
 @pytest.mark.parametrize("M,kernel,ws", [(1, 0, "auto"), (8, 3, "auto"), (300, 2, "auto"),
