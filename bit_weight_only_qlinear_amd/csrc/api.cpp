@@ -357,13 +357,15 @@ qp_status plan_forward(const qp_desc* d, qp::Desc* dd, int32_t x_dtype, int64_t 
     // The MFMA qGEMV runs one set of MFMAs per 16 activation rows instead of
     // one dot product per row and code pair.  Where it takes over from the
     // streaming qGEMV (timed on the decode layers): 2 rows for per-channel
-    // SYM4, 4 for Q6K, 5 for 8-bit affine codes (at 4 rows the qGEMV still
-    // wins: 19.2 vs 21.0 us on 14336 x 4096), 3 for the others.  Past 16
-    // rows the qGEMM, up to the K where its fp16 weights hold the output
-    // bound; beyond that the exact MFMA qGEMV in tiles of 16 activation rows.
+    // SYM4 and 4-bit affine codes (11.2 vs 12.5 us on 14336 x 4096), 3 for
+    // Q6K (20.8 vs 22.3 us on 8192 x 8192), 5 for 8-bit affine codes (at 4
+    // rows the qGEMV still wins: 19.1 vs 20.7 us), 3 for the others (Q4K at
+    // 2 rows: 24.7 on the qGEMV vs 35.4 us).  Past 16 rows the qGEMM, up to
+    // the K where its fp16 weights hold the output bound; beyond that the
+    // exact MFMA qGEMV in tiles of 16 activation rows.
     int64_t mfma_from = 3;
     if (dd->fmt == qp::SYM4 && dd->gs == dd->K) mfma_from = 2;
-    else if (dd->fmt == qp::Q6K) mfma_from = 4;
+    else if (dd->fmt == qp::AFFINE && dd->bits == 4) mfma_from = 2;
     else if (dd->fmt == qp::AFFINE && dd->bits == 8) mfma_from = 5;
     if (M >= mfma_from && M <= 16 && skinny_fits) *use = USE_SKINNY;
     else if (M <= 8 && gemv_fits) *use = USE_GEMV;

@@ -112,8 +112,8 @@ typedef enum { QP_F16 = 0, QP_BF16 = 1, QP_F32 = 2 } qp_dtype;
 
 /* Which kernel family qlinear_forward_kernel uses. */
 typedef enum {
-  QP_KERNEL_AUTO = 0,      /* M <= 8: qGEMV; from M = 2 (per-channel SYM4),
-                              4 (Q6K), 5 (8-bit AFFINE) or 3 (other formats)
+  QP_KERNEL_AUTO = 0,      /* M <= 8: qGEMV; from M = 2 (per-channel SYM4,
+                              4-bit AFFINE), 5 (8-bit AFFINE) or 3 (other formats)
                               up to M = 16: MFMA qGEMV when K % 128 == 0;
                               larger M: qGEMM up to
                               K = 8192 (per-channel SYM4: 2^20), the MFMA

@@ -345,9 +345,11 @@ def test_graph_replay_matches_eager(q, M, kernel, ws):
 
 
 def test_auto_dispatch_matches(q):
-    d = q.QDesc.affine(200, 1024)
-    for M in (1, 8, 9, 33):
-        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_AUTO, seed=M, with_bias=True)
+    """AUTO across its kernel boundaries: qGEMV, MFMA qGEMV (from 2 or 3
+    rows by format), qGEMM."""
+    for d in (q.QDesc.affine(200, 1024), q.QDesc.q6k(72, 1024), q.QDesc.affine(72, 1024, 8)):
+        for M in (1, 2, 3, 5, 8, 9, 33):
+            _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_AUTO, seed=M, with_bias=True)
 
 
 # ------------------------------------------------- full workload shapes
