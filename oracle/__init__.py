@@ -34,6 +34,10 @@ taken at their plainest reading; each is listed in the module that uses it.
     (convert.py: to_q4k, to_q6k).
   * The same page, "Ablation study": alternative scale / zero encodings
     (ablation.py: encode_value, dequant_f64, bits_per_weight).
+  * ExecuTorch PR #17235 (Metal int4 for Parakeet), review thread: the
+    "hqq" choice of quantization parameters for the affine int4 weights,
+    i.e. Half-Quadratic Quantization's zero-point optimisation
+    (hqq.py: quantize_affine_hqq, with the readings it lists).
 
 Parity status per function:
   quantize_* / pack_* / unpack_* / dequant_* / linear : pinned by the tests in
@@ -42,7 +46,11 @@ Parity status per function:
   equality).  a8w4 (quantize_activations, linear_a8w4): hand-worked tokens
   and dots, rounding invariants, exact rational brute force.  convert
   (to_q4k, to_q6k): hand-worked super-blocks, the lossless lattice case,
-  the half-step bound.  ablation: the table's bpw column, the uint8 case
+  the half-step bound.  hqq (quantize_affine_hqq, shrink_lp,
+  hqq_zero_step): hand-worked thresholds and zero updates, the
+  least-squares property of the update, no-iteration equality with the
+  pinned min/max quantizer, lattice losslessness, lower l_p error than
+  min/max.  ablation: the table's bpw column, the uint8 case
   against the pinned conversion, hand-worked lattice and rounding cases;
   its SNR values are parity unpinned (GGUF tensors), only the orderings.  snr_db: pinned by hand-worked closed forms; the
   pages' own SNR figures (GGUF tensors, not available) are not reproduced,
@@ -58,6 +66,7 @@ from .linear import linear_f64
 from .sizes import buffer_bytes, bits_per_weight
 from .metrics import snr_db, rel_l2, maxabs_bound
 from .a8w4 import quantize_activations, dequantize_activations, linear_a8w4
+from .hqq import quantize_affine_hqq
 
 __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "f16_bits_to_f32",
@@ -66,4 +75,5 @@ __all__ = [
     "dequant_f32", "dequant_out", "linear_f64", "buffer_bytes",
     "bits_per_weight", "snr_db", "rel_l2", "maxabs_bound",
     "quantize_activations", "dequantize_activations", "linear_a8w4",
+    "quantize_affine_hqq",
 ]
