@@ -5,6 +5,7 @@
 // whose weights are not divisible by 8); for the nested superscale formats
 // K % 256 == 0 and one step per 256-weight super-block, with detailed
 // messages on failure (ExecuTorch PR #20571 review: kernel-side validation).
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -201,6 +202,31 @@ qp_status qpack_quantize(const qp_desc* d, const float* W, const qp_weights* out
   return hip_status(qp::launch_quantize(dd, W, out->qweight, out->qweight_hi, out->scales,
                                         out->zeros, out->steps, (hipStream_t)stream),
                     "qpack_quantize launch");
+}
+
+qp_status qpack_quantize_hqq(const qp_desc* d, const float* W, const qp_weights* out,
+                             int32_t iters, float lp_norm, float beta, float kappa,
+                             void* stream) {
+  qp::Desc dd;
+  qp_status st = check_desc(d, &dd);
+  if (st != QP_OK) return st;
+  if (dd.fmt != qp::AFFINE)
+    return fail(QP_EUNSUPPORTED, "qpack_quantize_hqq takes the AFFINE format (got %d)", dd.fmt);
+  if (iters < 0 || iters > 10000)
+    return fail(QP_EINVAL, "iters must lie in [0, 10000] (got %d)", iters);
+  if (!(lp_norm > 0.f && lp_norm <= 1.f))
+    return fail(QP_EINVAL, "lp_norm must lie in (0, 1] (got %g)", (double)lp_norm);
+  if (!(beta > 0.f && std::isfinite(beta)))
+    return fail(QP_EINVAL, "beta must be positive and finite (got %g)", (double)beta);
+  if (!(kappa > 0.f && std::isfinite(kappa)))
+    return fail(QP_EINVAL, "kappa must be positive and finite (got %g)", (double)kappa);
+  if (!W) return fail(QP_EINVAL, "W is NULL");
+  if (!aligned16(W)) return fail(QP_EALIGN, "W is not 16-byte aligned");
+  if ((st = check_weights(dd, out, false)) != QP_OK) return st;
+  (void)hipGetLastError();
+  return hip_status(qp::launch_quantize_hqq(dd, W, out->qweight, out->scales, out->zeros, iters,
+                                            lp_norm, beta, kappa, (hipStream_t)stream),
+                    "qpack_quantize_hqq launch");
 }
 
 qp_status qpack_unpack_codes(const qp_desc* d, const qp_weights* w, void* codes, void* stream) {

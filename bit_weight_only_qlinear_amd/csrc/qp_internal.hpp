@@ -28,6 +28,9 @@ struct Bufs {
 hipError_t launch_quantize(const Desc& d, const float* W, void* qweight,
                            void* qweight_hi, void* scales, void* zeros,
                            void* steps, hipStream_t s);
+hipError_t launch_quantize_hqq(const Desc& d, const float* W, void* qweight, void* scales,
+                               void* zeros, int iters, float p, float beta, float kappa,
+                               hipStream_t s);
 hipError_t launch_unpack(const Desc& d, const Bufs& b, void* codes,
                          hipStream_t s);
 hipError_t launch_pack(const Desc& d, const void* codes, void* qweight,

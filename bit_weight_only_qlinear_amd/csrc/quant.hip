@@ -72,6 +72,94 @@ k_quant_affine(const float* __restrict__ W, uint32_t* __restrict__ qw,
   }
 }
 
+// ------------------------------------------------------------ AFFINE HQQ
+// One thread per group: the min/max scale and bias of k_quant_affine, then
+// the zero point chosen by Half-Quadratic Quantization (Badri and Shaji,
+// 2023; the "hqq" quantization-parameter option that ExecuTorch PR #17235's
+// review asks for on the Metal int4 affine weights).  The scale stays; the
+// zero point z (code units, w ~ (q - z) s, starting at -bias / s) alternates
+//   q = clamp(rint(w / s + z), 0, L),  e = w - (q - z) s,  err = sum |e|,
+//   W_e = sign(e) max(|e| - |e|^(p-1) / beta, 0)   (generalised soft threshold),
+//   z <- mean(q - (w - W_e) / s),  beta <- kappa beta,
+// and keeps the iterate with the smallest err (a strictly smaller one
+// replaces it; the start counts).  The kept z becomes the stored bias
+// meta(-z s) and the codes are rounded against the stored scale and bias
+// exactly as k_quant_affine does, so dequantization is unchanged.  Each step
+// is one fp32 operation in that order (-ffp-contract=off), |e|^(p-1) is
+// evaluated in fp64 and rounded once, the group sums run in ascending k.
+template <int BITS>
+__global__ void __launch_bounds__(kThreads)
+k_quant_affine_hqq(const float* __restrict__ W, uint32_t* __restrict__ qw,
+                   uint16_t* __restrict__ scales, uint16_t* __restrict__ biases,
+                   int64_t N, int64_t K, int gs, int meta_bf16, int iters, float p,
+                   float beta0, float kappa) {
+  const int64_t ng = K / gs;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= N * ng) return;
+  const int64_t n = g / ng, gi = g % ng;
+  const float* wr = W + n * K + gi * gs;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int k = 0; k < gs; ++k) {
+    lo = fminf(lo, wr[k]);
+    hi = fmaxf(hi, wr[k]);
+  }
+  lo = lo + 0.f;   // canonical +0
+  hi = hi + 0.f;
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  const uint32_t sb = meta_bf16 ? f32_to_bf16_rne(div_rn(hi - lo, qmax))
+                                : f32_to_f16_rne(div_rn(hi - lo, qmax));
+  uint32_t bb = meta_bf16 ? f32_to_bf16_rne(lo) : f32_to_f16_rne(lo);
+  const float s = meta_to_f32(sb, meta_bf16);
+  if (s != 0.f) {
+    const double pm1 = (double)p - 1.0;
+    float z = div_rn(-meta_to_f32(bb, meta_bf16), s);
+    float best_z = z, best_err = INFINITY, beta = beta0;
+    for (int t = 0; t <= iters; ++t) {
+      const bool upd = t < iters;
+      float err = 0.f, vsum = 0.f;
+      for (int k = 0; k < gs; ++k) {
+        const float w = wr[k];
+        const float q = clampf(rintf(div_rn(w, s) + z), 0.f, qmax);
+        const float e = w - (q - z) * s;
+        const float a = fabsf(e);
+        err = err + a;
+        if (upd) {
+          float we = 0.f;
+          if (a > 0.f) {
+            const float th = a - div_rn((float)pow((double)a, pm1), beta);
+            if (th > 0.f) we = copysignf(th, e);
+          }
+          vsum = vsum + (q - div_rn(w - we, s));
+        }
+      }
+      if (err < best_err) {
+        best_err = err;
+        best_z = z;
+      }
+      if (upd) {
+        z = div_rn(vsum, (float)gs);
+        beta = beta * kappa;
+      }
+    }
+    const float bias = (-best_z) * s + 0.f;
+    bb = meta_bf16 ? f32_to_bf16_rne(bias) : f32_to_f16_rne(bias);
+  }
+  scales[g] = (uint16_t)sb;
+  biases[g] = (uint16_t)bb;
+  const float b = meta_to_f32(bb, meta_bf16);
+  constexpr int per = 32 / BITS;
+  uint32_t* dst = qw + (n * K + gi * gs) / per;
+  for (int wi = 0; wi < gs / per; ++wi) {
+    uint32_t word = 0;
+    for (int j = 0; j < per; ++j) {
+      const float w = wr[wi * per + j];
+      const float q = (s == 0.f) ? 0.f : clampf(rintf(div_rn(w - b, s)), 0.f, qmax);
+      word |= (uint32_t)q << (BITS * j);
+    }
+    dst[wi] = word;
+  }
+}
+
 // ------------------------------------------------------------------ Q4K
 // One thread per super-block of 256 (8 groups of 32).
 __global__ void __launch_bounds__(kThreads)
@@ -533,6 +621,28 @@ hipError_t launch_quantize(const Desc& d, const float* W, void* qweight,
                        static_cast<const float*>(scales), static_cast<uint32_t*>(qweight), N,
                        K, (int64_t)d.gs);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_hqq(const Desc& d, const float* W, void* qweight, void* scales,
+                               void* zeros, int iters, float p, float beta, float kappa,
+                               hipStream_t s) {
+  const int64_t N = d.N, K = d.K;
+  const int64_t ng = N * (K / d.gs);
+  const int mb = d.meta == BF16;
+  auto* qw = static_cast<uint32_t*>(qweight);
+  auto* sc = static_cast<uint16_t*>(scales);
+  auto* bi = static_cast<uint16_t*>(zeros);
+  const dim3 grid(blocks_for(ng)), block(kThreads);
+  if (d.bits == 2)
+    hipLaunchKernelGGL(k_quant_affine_hqq<2>, grid, block, 0, s, W, qw, sc, bi, N, K, d.gs, mb,
+                       iters, p, beta, kappa);
+  else if (d.bits == 4)
+    hipLaunchKernelGGL(k_quant_affine_hqq<4>, grid, block, 0, s, W, qw, sc, bi, N, K, d.gs, mb,
+                       iters, p, beta, kappa);
+  else
+    hipLaunchKernelGGL(k_quant_affine_hqq<8>, grid, block, 0, s, W, qw, sc, bi, N, K, d.gs, mb,
+                       iters, p, beta, kappa);
   return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ def _load():
         "qpack_last_error": (ctypes.c_char_p, []),
         "qpack_sizes": (I32, [D, ctypes.POINTER(ctypes.c_size_t)]),
         "qpack_quantize": (I32, [D, P, W, P]),
+        "qpack_quantize_hqq": (I32, [D, P, W, I32, ctypes.c_float, ctypes.c_float,
+                                     ctypes.c_float, P]),
         "qpack_unpack_codes": (I32, [D, W, P, P]),
         "qpack_pack_codes": (I32, [D, P, W, P]),
         "qpack_dequantize": (I32, [D, W, P, I32, P]),
@@ -76,6 +78,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("qpack_abi_version", "qpack_last_error", "qpack_sizes", "qpack_quantize",
+            "qpack_quantize_hqq",
             "qpack_unpack_codes", "qpack_pack_codes", "qpack_dequantize",
             "qlinear_forward", "qlinear_forward_kernel", "qlinear_workspace_bytes",
             "qlinear_forward_ws", "qlinear_forward_static", "qpack_encode_nested",
@@ -181,6 +184,19 @@ def qpack_quantize(desc: QDesc, W, out=None):
         out = alloc_weights(desc, W.device)
     d, ws = desc.c(), _wstruct(out)
     _check(lib.qpack_quantize(ctypes.byref(d), _ptr(W), ctypes.byref(ws), _stream(W.device)))
+    return out
+
+
+def qpack_quantize_hqq(desc: QDesc, W, out=None, iters=20, lp_norm=0.7, beta=10.0,
+                       kappa=1.01):
+    """AFFINE only: W device fp32 [N, K] -> packed buffers, with the HQQ zero
+    point per group (see qpack_quantize_hqq in include/qlinear.h)."""
+    if out is None:
+        out = alloc_weights(desc, W.device)
+    d, ws = desc.c(), _wstruct(out)
+    _check(lib.qpack_quantize_hqq(ctypes.byref(d), _ptr(W), ctypes.byref(ws), int(iters),
+                                  float(lp_norm), float(beta), float(kappa),
+                                  _stream(W.device)))
     return out
 
 

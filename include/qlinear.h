@@ -166,6 +166,31 @@ qp_status qpack_sizes(const qp_desc* d, size_t bytes_out[5]);
 qp_status qpack_quantize(const qp_desc* d, const float* W, const qp_weights* out,
                          void* stream);
 
+/* AFFINE only: quantize W like qpack_quantize, but with the zero point
+ * (bias) of every group chosen by Half-Quadratic Quantization (HQQ, Badri
+ * and Shaji 2023), the "hqq" quantization-parameter option that ExecuTorch
+ * PR #17235's review ("Metal backend: Add Metal int4 quantization support
+ * to Parakeet") asks for on the Metal int4 affine weights.  The scale is the
+ * min/max scale of qpack_quantize; per group, starting from z0 = -bias/s in
+ * code units, `iters` updates
+ *     q = clamp(rint(w/s + z), 0, 2^b - 1),  e = w - (q - z)*s,
+ *     W_e = sign(e)*max(|e| - |e|^(lp_norm - 1)/beta, 0),
+ *     z <- mean(q - (w - W_e)/s),  beta <- kappa*beta
+ * run, the iterate with the smallest sum |e| is kept (the start included),
+ * the stored bias is meta(-z*s), and the codes are then rounded against the
+ * stored scale and bias as in qpack_quantize, so every forward kernel reads
+ * the result unchanged.  Every step is one fp32 operation in that order;
+ * |e|^(lp_norm - 1) is computed in fp64 and rounded once; group sums run in
+ * ascending k.  The method's defaults: iters 20, lp_norm 0.7, beta 10,
+ * kappa 1.01.  Errors: QP_EUNSUPPORTED for another format; QP_EINVAL for
+ * iters outside [0, 10000], lp_norm outside (0, 1], a non-positive or
+ * non-finite beta or kappa, and the checks of qpack_quantize.  Buffers as
+ * for qpack_quantize (qweight_hi and steps unused); asynchronous on
+ * `stream`.  Off the forward path: one thread per group. */
+qp_status qpack_quantize_hqq(const qp_desc* d, const float* W, const qp_weights* out,
+                             int32_t iters, float lp_norm, float beta, float kappa,
+                             void* stream);
+
 /* Expand the packed codes of `w` into `codes` (device [N, K] bytes): uint8
  * q for AFFINE and Q4K, int8 q for Q6K and SYM4 (SYM4 gives the int8 carrier
  * form of the a8w4 page, values in [-7, 7]). */

@@ -168,6 +168,29 @@ def test_concat_and_encode_validate(q):
                                      ctypes.byref(w4), None, None) == q.QP_EALIGN
 
 
+def test_quantize_hqq_validates(q):
+    """Host-side checks of qpack_quantize_hqq (no device access)."""
+    w = q._Weights(FAKE, None, FAKE, FAKE, None)
+    W = ctypes.c_void_p(FAKE)
+    d = q.QDesc.affine(64, 512).c()
+
+    def call(desc=d, Wp=W, iters=20, p=0.7, beta=10.0, kappa=1.01):
+        return q.lib.qpack_quantize_hqq(ctypes.byref(desc), Wp, ctypes.byref(w), iters, p, beta,
+                                        kappa, None)
+    assert call(desc=q.QDesc.q4k(64, 512).c()) == q.QP_EUNSUPPORTED and "AFFINE" in _err(q)
+    assert call(iters=-1) == q.QP_EINVAL and "iters" in _err(q)
+    assert call(iters=10001) == q.QP_EINVAL
+    assert call(p=0.0) == q.QP_EINVAL and "lp_norm" in _err(q)
+    assert call(p=1.5) == q.QP_EINVAL
+    assert call(beta=0.0) == q.QP_EINVAL and "beta" in _err(q)
+    assert call(beta=float("inf")) == q.QP_EINVAL
+    assert call(kappa=float("nan")) == q.QP_EINVAL and "kappa" in _err(q)
+    assert call(Wp=None) == q.QP_EINVAL
+    assert call(Wp=ctypes.c_void_p(FAKE + 4)) == q.QP_EALIGN
+    bad = q.QDesc.affine(64, 500).c()
+    assert call(desc=bad) != q.QP_OK
+
+
 def test_workspace_query_and_checks(q):
     n = ctypes.c_size_t(7)
     d = q.QDesc.affine(64, 512).c()
