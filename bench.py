@@ -152,6 +152,23 @@ def gemv_case(q, desc, W_np, M, x_bits, layers, steps, warmup):
     return res
 
 
+def copy_floor_case(nbytes, layers, steps, warmup):
+    """Calibration, not the target: a plain device-to-device copy moving
+    `nbytes` per launch (nbytes/2 read + nbytes/2 written), `layers`
+    distinct buffer pairs captured in one graph and timed exactly like the
+    qGEMV, so that it carries the same per-launch dispatch and ramp cost."""
+    import torch
+    n = nbytes // 2 // 4
+    src = [torch.ones(n, dtype=torch.float32, device="cuda") for _ in range(layers)]
+    dst = [torch.empty_like(a) for a in src]
+    fns = [(lambda a=a, b=b: b.copy_(a)) for a, b in zip(src, dst)]
+    wall, ev_ms = time_graph(fns, steps, warmup)
+    per_launch_s = ev_ms * 1e-3 / (steps * layers)
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(us_per_call=per_launch_s * 1e6, gbs=2 * n * 4 / per_launch_s / 1e9)
+
+
 def concat_case(q, K, Ns, x_bits, layers, steps, warmup):
     """Fused-N projections (e.g. q, k, v of one attention layer): the parts
     as separate forward calls against one forward over their qpack_concat_n
@@ -388,6 +405,14 @@ def main():
 
     extras = []
     qgemm = None
+    floor = copy_floor_case(head["bytes_per_call"], args.layers, max(20, args.steps // 4),
+                            args.warmup)
+    calibration = dict(workload="plain device copy moving the headline's bytes per launch "
+                                "(half read, half written), 32 distinct buffer pairs in one "
+                                "graph, timed like the qGEMV (torch copy_)",
+                       us_per_call=round(floor["us_per_call"], 3),
+                       gbs=round(floor["gbs"], 1), frac=round(floor["gbs"] / HBM_PEAK_GBS, 4))
+    log("calibration", calibration)
     if not args.quick:
         for bits in (2, 8):
             d = q.QDesc.affine(N, K, bits, 64, "bf16")
@@ -490,6 +515,7 @@ def main():
             "us_per_launch": round(head["us_per_call"], 3),
             "algorithmic_bytes": head["bytes_per_call"],
             "traffic": measured_traffic(),
+            "calibration": calibration,
         },
         "cpu_baseline": cpu,
         "qgemm": qgemm,
