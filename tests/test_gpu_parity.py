@@ -152,6 +152,23 @@ def test_gemv_forward(q, N, K, M):
                           with_bias=(i % 2 == 0))
 
 
+# Rows of C = 64 q + 32 chunks of 16 code bytes (32 codes per chunk for 4-
+# and 6-bit codes, 16 for 8-bit, 64 for 2-bit): the last chunk slot of every
+# lane is half empty (masked lanes); 32, 96 and 160 chunks, even and odd N.
+HALF_SLOT_SHAPES = [(2, 1024), (78, 1024), (300, 3072), (514, 5120), (513, 5120), (96, 512),
+                    (40, 1536), (30, 2560), (64, 2048), (22, 6144)]
+
+
+@pytest.mark.parametrize("N,K", HALF_SLOT_SHAPES)
+def test_gemv_half_filled_slots(q, N, K):
+    for i, d in enumerate(_descs(q, N, K)):
+        for xdt, ydt in [("bf16", "f32"), ("bf16", "bf16"), ("f16", "f16")]:
+            print("gemv half slots", _id(d), xdt, ydt, flush=True)
+            _forward_case(q, d, 1, xdt, ydt, q.QP_KERNEL_GEMV, seed=N * 13 + K + i,
+                          with_bias=(i % 2 == 1))
+        _forward_case(q, d, 2, "bf16", "f32", q.QP_KERNEL_GEMV, seed=N + K + i, with_bias=True)
+
+
 @pytest.mark.parametrize("N,K", [(1, 256), (31, 384), (77, 1024), (300, 4096), (513, 5120)])
 @pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 11, 16, 17, 40])
 def test_gemv_mfma_forward(q, N, K, M):
