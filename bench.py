@@ -236,8 +236,28 @@ def gemm_case(q, desc, W_np, x_bits, steps, warmup, warmup_s=0.3):
     per = ev_ms * 1e-3 / steps
     flops = 2.0 * M * desc.N * desc.K
     tf = flops / per / 1e12
+    # the C call with no workspace argument (qlinear_forward), eager: it
+    # takes its workspace from the library's pool (not under capture)
+    import ctypes
+    d, ws = desc.c(), q._wstruct(w)
+    yd = q.DTYPE_IDS["bf16"]
+
+    def plain():
+        st = q.lib.qlinear_forward(ctypes.byref(d), q._ptr(xd), yd, M, ctypes.byref(ws), None,
+                                   q._ptr(y), yd, q._stream(xd.device))
+        assert st == q.QP_OK, q.lib.qpack_last_error()
+    for _ in range(20):
+        plain()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        plain()
+    ev1.record()
+    torch.cuda.synchronize()
+    plain_us = ev0.elapsed_time(ev1) * 1e3 / steps
     return dict(flops_per_call=flops, us_per_call=per * 1e6, tflops=tf,
-                frac=tf / MFMA_F16_PEAK_TFLOPS, tok_s_per_layer=M / per)
+                frac=tf / MFMA_F16_PEAK_TFLOPS, tok_s_per_layer=M / per, plain_c_us=plain_us)
 
 
 def _blas_threads():
@@ -475,7 +495,10 @@ def main():
                      peak=MFMA_F16_PEAK_TFLOPS, frac=round(r["frac"], 4),
                      us_per_call=round(r["us_per_call"], 2),
                      tok_s_per_layer=round(r["tok_s_per_layer"], 1),
-                     warmup="untimed graph replays for >= 0.3 s (clocks settle under MFMA load)")
+                     warmup="untimed graph replays for >= 0.3 s (clocks settle under MFMA load)",
+                     plain_c_call_us=round(r["plain_c_us"], 2),
+                     plain_c_call="qlinear_forward (the C call without a workspace argument: "
+                                  "workspace from the library's pool), eager launches")
         log("qgemm", qgemm)
         del w5
 

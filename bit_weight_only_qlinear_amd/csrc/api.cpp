@@ -10,6 +10,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/qlinear.h"
@@ -407,6 +408,45 @@ qp_status plan_forward(const qp_desc* d, qp::Desc* dd, int32_t x_dtype, int64_t 
 
 }  // namespace
 
+namespace {
+
+// Memory pool of each device for qlinear_forward's stream-ordered
+// workspace, created on first use with that device current; it keeps what
+// it has served (release threshold at the maximum), so later calls reuse
+// that memory.  Held until the process ends.
+constexpr int kPoolDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kPoolDevices];
+
+hipError_t forward_pool(hipMemPool_t* out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kPoolDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pool[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    e = hipMemPoolCreate(&p, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = ~uint64_t(0);
+    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) {
+      (void)hipMemPoolDestroy(p);
+      return e;
+    }
+    g_pool[dev] = p;
+  }
+  *out = g_pool[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
 extern "C" {
 
 qp_status qlinear_workspace_bytes(const qp_desc* d, int32_t x_dtype, int64_t M, int32_t kernel,
@@ -503,6 +543,33 @@ qp_status qlinear_forward_kernel(const qp_desc* d, const void* x, int32_t x_dtyp
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype, int64_t M,
                           const qp_weights* w, const void* bias, void* y, int32_t y_dtype,
                           void* stream) {
+  // Where the qGEMM's 224-row tiling wants staged activations, take the
+  // workspace stream-ordered from the library's pool and give it back on the
+  // same stream after the qGEMM (no other call, on any stream, can see it in
+  // between).  Under stream capture, or if the pool cannot serve it, run the
+  // workspace-free tiling (same result, slower).
+  qp::Desc dd;
+  Use use;
+  size_t nbytes[5];
+  qp_status st = plan_forward(d, &dd, x_dtype, M, QP_KERNEL_AUTO, &use, nbytes);
+  if (st != QP_OK) return st;
+  const size_t need = use == USE_GEMM ? qp::gemm_workspace_bytes(dd, M) : 0;
+  if (need > 0) {
+    const hipStream_t s = (hipStream_t)stream;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipMemPool_t pool = nullptr;
+    void* ws = nullptr;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone &&
+        forward_pool(&pool) == hipSuccess &&
+        hipMallocFromPoolAsync(&ws, need, pool, s) == hipSuccess) {
+      st = qlinear_forward_ws(d, x, x_dtype, M, w, bias, y, y_dtype, QP_KERNEL_AUTO, ws, need,
+                              stream);
+      const hipError_t e = hipFreeAsync(ws, s);
+      if (st == QP_OK && e != hipSuccess) return hip_status(e, "workspace release");
+      return st;
+    }
+    (void)hipGetLastError();
+  }
   return qlinear_forward_kernel(d, x, x_dtype, M, w, bias, y, y_dtype, QP_KERNEL_AUTO, stream);
 }
 

@@ -263,7 +263,16 @@ qp_status qpack_dequantize(const qp_desc* d, const qp_weights* w, void* W_out,
  * finite bf16 activation is taken.  To hold the per-row exponents without a
  * workspace the qGEMM writes them into y before it computes; y's contents
  * are undefined until the call completes.  QP_KERNEL_AUTO picks by M and K as
- * listed under qp_kernel. */
+ * listed under qp_kernel.
+ * Where the qGEMM's 224-row tiling applies (qlinear_workspace_bytes > 0),
+ * this call takes that workspace stream-ordered from a memory pool the
+ * library keeps per device (created on first use, keeping what it served
+ * for reuse until the process ends: about 2 (K + 2) bytes per activation
+ * row) and returns it on `stream` after the qGEMM, so calls on different
+ * streams never share it; under stream capture, or when the pool cannot
+ * serve the request, it runs the workspace-free 256-row tiling instead
+ * (same contract, slower).  Callers that manage memory themselves use
+ * qlinear_forward_ws; callers that cannot allocate, qlinear_forward_static. */
 qp_status qlinear_forward(const qp_desc* d, const void* x, int32_t x_dtype,
                           int64_t M, const qp_weights* w, const void* bias,
                           void* y, int32_t y_dtype, void* stream);

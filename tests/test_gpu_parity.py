@@ -419,3 +419,55 @@ def test_full_decode_8k(q, M):
 def test_full_prefill(q):
     d = q.QDesc.affine(14336, 4096, 4, 64, "bf16")
     _full(q, "prefill_affine", d, 2048, q.QP_KERNEL_AUTO, "bf16", "bf16")
+
+
+def test_plain_forward_pool_workspace(q):
+    """The C call qlinear_forward (no workspace argument) at qGEMM shapes
+    takes the staged-activation workspace stream-ordered from the library's
+    pool: bit-identical to qlinear_forward_ws with a caller workspace on two
+    calls in a row (the second smaller, reusing the pool), within the bound
+    against the oracle; under graph capture it runs the workspace-free
+    tiling, and the replays equal that tiling's eager result."""
+    import ctypes
+    N, K = 448, 1024
+    d = q.QDesc.affine(N, K, 4, 64, "bf16")
+    W = _weights(N, K, 91)
+    f = qformat_of(d)
+    buf = q.qpack_quantize(d, torch.from_numpy(W).cuda())
+    qz = oracle.quantize(W, f)
+    w64 = oracle.dequant_f64(qz, f)
+    ws = q._wstruct(buf)
+
+    def plain(xd, y):
+        return q.lib.qlinear_forward(ctypes.byref(d.c()), q._ptr(xd), q.DTYPE_IDS["bf16"],
+                                     xd.shape[0], ctypes.byref(ws), None, q._ptr(y),
+                                     q.DTYPE_IDS["f32"], q._stream(xd.device))
+
+    rng = np.random.default_rng(5)
+    for M in (300, 100):
+        assert q.workspace_bytes(d, M, "bf16", q.QP_KERNEL_AUTO) > 0
+        xb = synth.draw_activations(rng, M, K, "bf16")
+        xd = to_dev_bits(xb, "bf16")
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        assert plain(xd, y) == q.QP_OK, q.lib.qpack_last_error()
+        y_ws = q.qlinear_forward(d, xd, buf, y_dtype="f32")   # caller (torch) workspace
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ws), M
+        x64 = oracle.decode_activations(xb, "bf16")
+        check_linear(y, oracle.linear_f64(x64, qz, f, w64=w64), x64, np.abs(w64).max(), K, "f32")
+    # captured: the workspace-free tiling
+    y_free = q.qlinear_forward(d, xd, buf, y_dtype="f32", workspace=None)
+    torch.cuda.synchronize()
+    yg = torch.empty_like(y_free)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        assert plain(xd, yg) == q.QP_OK
+    for _ in range(3):
+        yg.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y_free)
+
