@@ -183,6 +183,18 @@ def test_gemv_mfma_forward(q, N, K, M):
                           with_bias=(i % 2 == 1))
 
 
+@pytest.mark.parametrize("M", [3, 16])
+def test_gemv_mfma_many_blocks(q, M):
+    """The MFMA qGEMV with more blocks than two per CU (N = 16416 rows: 513
+    blocks of 32 rows) and a short K, on six formats."""
+    N, K = 16416, 256
+    D = q.QDesc
+    for i, d in enumerate([D.affine(N, K, 4, 64, "bf16"), D.affine(N, K, 8, 32, "f16"),
+                           D.q4k(N, K), D.q6k(N, K), D.sym4(N, K), D.sym4(N, K, 64)]):
+        print("gemv_mfma many blocks", _id(d), M, flush=True)
+        _forward_case(q, d, M, "bf16", "f32", q.QP_KERNEL_GEMV_MFMA, seed=M + i, with_bias=(i % 2 == 0))
+
+
 @pytest.mark.parametrize("fmt", ["affine32", "affine64", "affine2", "affine8", "q4k", "q6k",
                                  "sym4", "sym4g32"])
 def test_large_k_exact(q, fmt):
