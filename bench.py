@@ -386,8 +386,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sharding is described in the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(its layers would shard along N, one slice of rows per GPU). "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
