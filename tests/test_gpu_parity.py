@@ -183,6 +183,21 @@ def test_gemv_mfma_forward(q, N, K, M):
                           with_bias=(i % 2 == 1))
 
 
+@pytest.mark.parametrize("fmt", ["affine4", "affine2", "affine8", "q4k", "q6k", "sym4", "sym4g64"])
+def test_gemm_more_tiles_than_cus(q, fmt):
+    """The 224-row qGEMM with 320 tiles (M = 2048, N = 8960), more blocks
+    than CUs, on seven formats: every output against the oracle, bf16 and
+    fp32 outputs."""
+    N, K, M = 8960, 256, 2048
+    d = {"affine4": q.QDesc.affine(N, K, 4, 64), "affine2": q.QDesc.affine(N, K, 2, 32, "f16"),
+         "affine8": q.QDesc.affine(N, K, 8, 64), "q4k": q.QDesc.q4k(N, K), "q6k": q.QDesc.q6k(N, K),
+         "sym4": q.QDesc.sym4(N, K), "sym4g64": q.QDesc.sym4(N, K, 64)}[fmt]
+    assert q.workspace_bytes(d, M, "bf16", q.QP_KERNEL_GEMM) > 0   # the 224-row tiling
+    for ydt in ("bf16", "f32"):
+        print("gemm many tiles", _id(d), ydt, flush=True)
+        _forward_case(q, d, M, "bf16", ydt, q.QP_KERNEL_GEMM, seed=len(fmt), with_bias=ydt == "f32")
+
+
 @pytest.mark.parametrize("M", [3, 16])
 def test_gemv_mfma_many_blocks(q, M):
     """The MFMA qGEMV with more blocks than two per CU (N = 16416 rows: 513
