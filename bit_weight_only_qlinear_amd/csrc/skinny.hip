@@ -256,6 +256,15 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* ld
 // 0 and 2: codes 0-3 in byte 0, codes 4-7 in byte 2 (2 bits each).
 __device__ __forceinline__ uint32_t spread2(uint32_t p) { return (p & 0xFFu) | ((p & 0xFF00u) << 8); }
 
+// (a & m) | c in one v_and_or_b32 (LLVM otherwise builds two ANDs and a
+// three-way OR for the Q6K code pairs; the masks go in SGPRs, as gfx9 VOP3
+// takes no literal)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
+  return r;
+}
+
 // B operand of one MFMA step: the lane's 8 codes in element order
 // (0, 4, 1, 5, 2, 6, 3, 7), each MAG + u exactly.
 template <int KIND, bool XBF16>
@@ -282,14 +291,27 @@ __device__ __forceinline__ uint4 code_frag(uint32_t w, uint32_t w2, uint32_t hq)
     }
   } else if constexpr (KIND == S_Q6K) {
     const uint32_t q = spread2(hq);   // high 2 bits of the 8 codes
+    // bits 2e, 2e + 1 of each half of q moved to bits 4, 5, joined with the
+    // magic, then with the low nibbles: two v_and_or_b32 per pair
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p[e] = ((w >> (4 * e)) & 0x000F000Fu) | (((q >> (2 * e)) & 0x00030003u) << 4) | magic;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t qs = e < 2 ? q << (4 - 2 * e) : q >> (2 * e - 4);
+      p[e] = and_or(w >> (4 * e), 0x000F000Fu, and_or(qs, 0x00300030u, magic));
+    }
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = ((w >> (4 * e)) & 0x000F000Fu) | magic;
   }
   return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// The same with per-lane byte selectors: (s0, s1) = (0x05040100,
+// 0x07060302) give act_frag's element order, 0x0C0C0C0C gives zeros
+// (v_perm_b32 selector byte 12 is the constant 0x00) -- the Q6K step's
+// half-masked operands without a select per register.
+__device__ __forceinline__ uint4 act_frag_sel(uint4 v, uint32_t s0, uint32_t s1) {
+  return make_uint4(__builtin_amdgcn_perm(v.z, v.x, s0), __builtin_amdgcn_perm(v.z, v.x, s1),
+                    __builtin_amdgcn_perm(v.w, v.y, s0), __builtin_amdgcn_perm(v.w, v.y, s1));
 }
 
 // A operand: 8 activations (two per word, column order) in the same element
@@ -349,6 +371,9 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
   const int KB = (int)(a.K / kSxCols);
 
   const uint32_t one = XBF16 ? 0x3F803F80u : 0x3C003C00u;
+  // Q6K: v_perm selectors of the lane's half-masked activation operands
+  const uint32_t selL0 = g < 2 ? 0x05040100u : 0x0C0C0C0Cu, selL1 = g < 2 ? 0x07060302u : 0x0C0C0C0Cu;
+  const uint32_t selH0 = g < 2 ? 0x0C0C0C0Cu : 0x05040100u, selH1 = g < 2 ? 0x0C0C0C0Cu : 0x07060302u;
   const uint4 ONES = make_uint4(one, one, one, one);
   // acc[i][v]: activation row 4 g + v, weight row 16 i + r16
   float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -413,11 +438,10 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
     }
     sfor<4>([&](auto TT) {
       constexpr int t = decltype(TT)::value;
-      const uint4 A = act_frag(s.x[t]);
       if constexpr (KIND == S_Q6K) {
         // two groups per step: lane groups 0-1 (group 2 t), 2-3 (2 t + 1)
-        const uint4 Z = make_uint4(0, 0, 0, 0);
-        const uint4 Al = g < 2 ? A : Z, Ah = g < 2 ? Z : A;
+        const uint4 Al = act_frag_sel(s.x[t], selL0, selL1);
+        const uint4 Ah = act_frag_sel(s.x[t], selH0, selH1);
         float4_t Dh[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -431,6 +455,7 @@ __global__ void __launch_bounds__(64 * kSxWaves) k_skinny(SxArgs a) {
         epilogue(s, 2 * t + 1, Dh, DX);
         D[0] = D[1] = float4_t{0.f, 0.f, 0.f, 0.f};
       } else {
+        const uint4 A = act_frag(s.x[t]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           D[i] = mfma<XBF16>(A, code_frag<KIND, XBF16>(W[i][t], KIND == S_AFF8 ? W2[i][t] : 0u, 0u),
