@@ -256,15 +256,6 @@ __device__ __forceinline__ void sx_load(const SxArgs& a, const unsigned char* ld
 // 0 and 2: codes 0-3 in byte 0, codes 4-7 in byte 2 (2 bits each).
 __device__ __forceinline__ uint32_t spread2(uint32_t p) { return (p & 0xFFu) | ((p & 0xFF00u) << 8); }
 
-// (a & m) | c in one v_and_or_b32 (LLVM otherwise builds two ANDs and a
-// three-way OR for the Q6K code pairs; the masks go in SGPRs, as gfx9 VOP3
-// takes no literal)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-  return r;
-}
-
 // B operand of one MFMA step: the lane's 8 codes in element order
 // (0, 4, 1, 5, 2, 6, 3, 7), each MAG + u exactly.
 template <int KIND, bool XBF16>
@@ -291,13 +282,9 @@ __device__ __forceinline__ uint4 code_frag(uint32_t w, uint32_t w2, uint32_t hq)
     }
   } else if constexpr (KIND == S_Q6K) {
     const uint32_t q = spread2(hq);   // high 2 bits of the 8 codes
-    // bits 2e, 2e + 1 of each half of q moved to bits 4, 5, joined with the
-    // magic, then with the low nibbles: two v_and_or_b32 per pair
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t qs = e < 2 ? q << (4 - 2 * e) : q >> (2 * e - 4);
-      p[e] = and_or(w >> (4 * e), 0x000F000Fu, and_or(qs, 0x00300030u, magic));
-    }
+    for (int e = 0; e < 4; ++e)
+      p[e] = ((w >> (4 * e)) & 0x000F000Fu) | (((q >> (2 * e)) & 0x00030003u) << 4) | magic;
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = ((w >> (4 * e)) & 0x000F000Fu) | magic;
