@@ -73,7 +73,7 @@ def round_out(y_ref, ydt):
     return y32.astype(np.float64)
 
 
-def check_linear(y_dev, y_ref, x64, wmax, K, ydt, rel=2e-3, extra=None):
+def check_linear(y_dev, y_ref, x64, wmax, K, ydt, rel=2e-3):
     """The layer's tolerance: rel-L2 <= 2e-3 and per element
     |y - y_ref| <= 1e-2 * ||x_m|| * max|w| / sqrt(K) (+ half an output ulp
     for fp16 / bf16 outputs, the rounding of the result itself).
@@ -89,8 +89,6 @@ def check_linear(y_dev, y_ref, x64, wmax, K, ydt, rel=2e-3, extra=None):
     if ydt != "f32" and y.size < 4096:
         rel = rel + oracle.rel_l2(round_out(y_ref, ydt), y_ref)
     bound = oracle.maxabs_bound(x64, wmax, K)
-    if extra is not None:
-        bound = bound + extra
     if ydt != "f32":
         bound = bound + 0.5 * ulp(y_ref, ydt)
     err = np.abs(y - y_ref)
