@@ -304,7 +304,8 @@ def test_gemm_forward(q, N, K, M):
 def test_gemm_workspace_tilings_agree(q, N, K, M):
     """224-row tiles (staged activations) and 256-row tiles: same fp16
     operands, fp32 sums in another order; a workspace full of NaN bytes
-    checks that the staging writes every byte the kernel reads."""
+    checks that the staging writes every byte the kernel reads.  Both
+    results are also held to the oracle's product."""
     for i, d in enumerate(_descs(q, N, K)):
         for xdt in ("bf16", "f16"):
             print("gemm workspace", _id(d), M, xdt, flush=True)
@@ -323,11 +324,19 @@ def test_gemm_workspace_tilings_agree(q, N, K, M):
             torch.cuda.synchronize()
             assert torch.isfinite(y1).all()
             assert torch.equal(y1, y2)
-            # |difference| <= K * 2^-23 * sum |w x| bounds two fp32 summation orders
-            wd = q.qpack_dequantize(d, buf, "f16").float()
-            xf = xd.float()
-            bound = K * 2.0 ** -23 * (xf.abs() @ wd.abs().T) + 1e-30
-            assert ((y0 - y1).abs() <= bound).all()
+            f = qformat_of(d)
+            qz = oracle.quantize(W, f)
+            w64 = oracle.dequant_f64(qz, f)
+            x64 = oracle.decode_activations(xb, xdt)
+            y_ref = oracle.linear_f64(x64, qz, f, w64=w64)
+            check_linear(y0, y_ref, x64, np.abs(w64).max(), K, "f32")
+            check_linear(y1, y_ref, x64, np.abs(w64).max(), K, "f32")
+            # |difference| <= K * 2^-23 * sum |w x| bounds two fp32 summation
+            # orders of the same products; the sum is taken over the oracle's
+            # w and x, 1% above it covering the fp16 rounding of the operands
+            bound = 1.01 * K * 2.0 ** -23 * (np.abs(x64) @ np.abs(w64).T) + 1e-30
+            diff = (y0 - y1).abs().double().cpu().numpy()
+            assert np.all(diff <= bound)
 
 
 def test_gemm_workspace_long_rows(q):
