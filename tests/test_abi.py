@@ -226,3 +226,24 @@ def test_workspace_query_and_checks(q):
     assert fwd(FAKE, 16) == q.QP_EINVAL and "workspace too small" in _err(q)
     assert fwd(FAKE + 8, 1 << 20) == q.QP_EALIGN and "workspace" in _err(q)
     assert fwd(FAKE, 16, M=0) == q.QP_ESHAPE
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No fallback: with libqlinear.so absent, importing the binding raises
+    (checked in a child process that hides the built file)."""
+    import subprocess
+    import sys
+    code = ("import os\n"
+            "real = os.path.exists\n"
+            "os.path.exists = lambda p: False if str(p).endswith('libqlinear.so') else real(p)\n"
+            "try:\n"
+            "    import bit_weight_only_qlinear_amd.qlinear\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "    raise SystemExit(3)\n"
+            "raise SystemExit(0)\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=root,
+                       timeout=120)
+    assert r.returncode == 3, r.stdout + r.stderr
+    assert "missing" in r.stdout
